@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step is one pass of the whole path over one batch: a mixed step whose front is
+the standard decode batch (64 cached rows, 16 key / 32 value heads, d_k = d_v = 128,
+bf16 q/k/v, fp32 states in a 256-slot cache) and whose prefill part is the long
+prefill (16 sequences x 8192 tokens, same heads, zero initial states, states exported
+on the 1088-token prefix-cache grid).  The step is issued as its three stages --
+gdn_recurrent_decode, gdn_chunk_prefill_transform, gdn_chunk_prefill_scan -- which is
+exactly what gdn_mixed_step enqueues (checked bitwise before timing), so that HIP
+events on the launch stream time each stage.  Inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line: value = prefill tokens per second of the whole step; the
+decode part's state bandwidth and its fraction of the 8 TB/s HBM peak; the dominant
+kernel's roofline; and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s + decode state GB/s (frac of HBM peak) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+CHUNK = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
+                    help="prefill sequences (of 16) the oracle runs for the CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic_flops_per_token(H_k, H_v, d_k, d_v, C=CHUNK):
+    """Flops per prefill token of the chunked form, triangles counted once, K K^T and
+    Q K^T once per key head: H_k 2 C d_k + H_v (C (d_k + d_v) + C d_v + 6 d_k d_v)."""
+    return H_k * 2 * C * d_k + H_v * (C * (d_k + d_v) + C * d_v + 6 * d_k * d_v)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_rule_amd import binding
+    from gated_deltanet_rule_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    wd = W.config(1)                                           # decode batch
+    wp = W.config(4, fill_pool=False)                          # long prefill
+    H_k, H_v, d_k, d_v = wd.H_k, wd.H_v, wd.d_k, wd.d_v
+    B, N = wd.num_decode_rows, wp.num_seqs
+    Tp = wp.prefill_tokens
+    bf = torch.bfloat16
+
+    def cat(name, dtype):
+        a = torch.from_numpy(getattr(wd, name)).to(dev, dtype)
+        b = torch.from_numpy(getattr(wp, name)).to(dev, dtype)
+        return torch.cat([a, b]).contiguous()
+
+    q, k, v = cat("q", bf), cat("k", bf), cat("v", bf)
+    g, beta = cat("g", torch.float32), cat("beta", torch.float32)
+    num_slots = wd.pool.shape[0] + N
+    pool = torch.empty((num_slots, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    pool[:wd.pool.shape[0]] = torch.from_numpy(wd.pool).to(dev)
+    pool[wd.pool.shape[0]:] = 0
+    o = torch.empty_like(v)
+    i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32), device=dev)
+    slot_in, slot_out = i32(wd.slot_in), i32(wd.slot_out)
+    cu = i32(wp.cu_seqlens())
+    init_slot = i32(np.full(N, -1))
+    final_slot = i32(np.arange(wd.pool.shape[0], num_slots))
+    grid = wp.export_grid
+    offs = binding.export_offsets(wp.lengths, None, grid)
+    exp_offs = i32(offs)
+    exports = torch.empty((offs[-1], H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    ws = binding.alloc_workspace(H_v, bf, N, Tp, dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+
+    dq, dk_, dv_, dg, db, do = q[:B], k[:B], v[:B], g[:B], beta[:B], o[:B]
+    pq, pk, pv, pg, pb, po = q[B:], k[B:], v[B:], g[B:], beta[B:], o[B:]
+    pre = dict(scale=wp.scale, workspace=ws, export_grid=grid, export_states=exports, export_offsets=exp_offs)
+
+    def stage_decode():
+        binding.gdn_recurrent_decode(dq, dk_, dv_, dg, db, do, pool, slot_in, slot_out, scale=wd.scale)
+
+    def stage_transform():
+        binding.gdn_chunk_prefill_transform(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
+
+    def stage_scan():
+        binding.gdn_chunk_prefill_scan(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
+
+    # the staged step is the mixed step: check bitwise once, from the same pool
+    pool0 = pool.clone()
+    binding.gdn_mixed_step(q, k, v, g, beta, o, pool, slot_in, slot_out, cu, init_slot, final_slot, **pre)
+    torch.cuda.synchronize()
+    ref = (o.clone(), pool.clone(), exports.clone())
+    pool.copy_(pool0)
+    stage_decode(); stage_transform(); stage_scan()
+    torch.cuda.synchronize()
+    same = torch.equal(o, ref[0]) and torch.equal(pool, ref[1]) and torch.equal(exports, ref[2])
+    if not same:
+        print("staged step differs from gdn_mixed_step", file=sys.stderr)
+        sys.exit(1)
+    del pool0, ref
+
+    for _ in range(args.warmup):
+        stage_decode(); stage_transform(); stage_scan()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        stage_decode()
+        ev[i][1].record()
+        stage_transform()
+        ev[i][2].record()
+        stage_scan()
+        ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    t_tr = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    t_scan = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    # ---- figures
+    value = Tp / (ms_step * 1e-3)
+    dec_bytes = 2 * 4 * d_k * d_v * B * H_v                # fp32 state read + write per (row, head)
+    dec_gbps = dec_bytes / (t_dec * 1e-3) / 1e9
+    f_tok = algorithmic_flops_per_token(H_k, H_v, d_k, d_v)
+    kkt_tok = H_k * CHUNK * d_k                            # K K^T lower half, in the transform stage
+    scan_flops = (f_tok - kkt_tok) * Tp
+    scan_tflops = scan_flops / (t_scan * 1e-3) / 1e12
+    prefill_ms = t_tr + t_scan
+    kernels = {
+        "decode": {"ms": round(t_dec, 5), "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                   "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": dec_bytes},
+        "prefill_scan": {"ms": round(t_scan, 4), "bound": "mfma", "achieved": round(scan_tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / BF16_PEAK_TFLOPS, 4),
+                         "flops_per_launch": scan_flops},
+        "prefill_transform": {"ms": round(t_tr, 4)},
+    }
+    dominant = max(("decode", t_dec), ("prefill_scan", t_scan), ("prefill_transform", t_tr), key=lambda x: x[1])[0]
+    roof = kernels["prefill_scan"] if dominant != "decode" else kernels["decode"]
+    roofline = {"kernel": "chain_kernel (gdn_chunk_prefill_scan)" if roof is kernels["prefill_scan"]
+                else "decode_kernel (gdn_recurrent_decode)",
+                "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"], "unit": roof["unit"],
+                "frac": roof["frac"], "traffic": None}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mixed step: 64 cached decode rows (256-slot fp32 state cache) ahead of 16 x 8192-token "
+                               "prefills exporting states every 1088 tokens; 16 key / 32 value heads, d_k = d_v = 128, "
+                               "bf16 q/k/v, fp32 gates and states",
+                   "global_batch": B + N, "seq_len": 8192, "prefill_tokens": Tp, "decode_rows": B,
+                   "parallelism": "single GPU"},
+        "decode": {"state_GB_per_s": round(dec_gbps, 1), "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "ms": round(t_dec, 5), "state_bytes": dec_bytes},
+        "prefill": {"tokens_per_s": round(Tp / (prefill_ms * 1e-3), 1), "ms": round(prefill_ms, 4),
+                    "mfma_frac": round(f_tok * Tp / (prefill_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "flops_per_token": f_tok},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wp, wd, args.cpu_sample_seqs)
+    print("input generation %.1f s; step %.3f ms = decode %.4f + transform %.4f + scan %.4f ms" % (
+        gen_s, ms_step, t_dec, t_tr, t_scan), file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wp, wd, n_seqs):
+    """The oracle as it stands (fp64 sequential recurrence, OpenMP over (sequence,
+    head) units) on a bounded sample of the same workload."""
+    import oracle
+    n_seqs = max(1, min(n_seqs, wp.num_seqs))
+    L = wp.lengths[0]
+    T = n_seqs * L
+    cu = np.arange(n_seqs + 1, dtype=np.int32) * L
+    t0 = time.perf_counter()
+    oracle.prefill(wp.q[:T], wp.k[:T], wp.v[:T], wp.g[:T], wp.beta[:T], cu, scale=wp.scale,
+                   export_grid=wp.export_grid)
+    pre_s = time.perf_counter() - t0
+    B = wd.num_decode_rows
+    si = wd.slot_in
+    compact = wd.pool[si].astype(np.float64)
+    idx = np.arange(B, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, compact, idx, idx, scale=wd.scale)
+    dec_s = time.perf_counter() - t0
+    dec_bytes = 2 * 4 * wd.d_k * wd.d_v * B * wd.H_v
+    return {"value": round(T / pre_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "prefill of %d of the 16 sequences (%d tokens, all 32 heads, exports on the 1088 grid) "
+                      "in %.1f s; decode of the 64-row batch in %.3f s" % (n_seqs, T, pre_s, dec_s),
+            "decode_state_GB_per_s": round(dec_bytes / dec_s / 1e9, 3)}
+
+
+if __name__ == "__main__":
+    main()

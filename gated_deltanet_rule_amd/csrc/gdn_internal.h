@@ -1,0 +1,65 @@
+// gdn_internal.h -- launcher interface between the C ABI layer (gdn_api.cpp) and the
+// gfx950 kernels (gdn_decode.hip, gdn_prefill.hip).  Host-side declarations only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Packed single-token decode over cached rows.
+struct DecodeArgs {
+    int H_k, H_v, d_k, d_v, dtype;
+    float scale;
+    int num_rows;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    void* o;
+    float* pool;
+    int num_slots;
+    const int32_t* slot_in;
+    const int32_t* slot_out;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Chunked prefill over packed variable-length sequences.
+struct PrefillArgs {
+    int H_k, H_v, d_k, d_v, dtype;
+    float scale;
+    int num_seqs;
+    int64_t total_tokens;
+    const int32_t* cu_seqlens;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    void* o;
+    float* pool;
+    int num_slots;
+    const int32_t* init_slot;
+    const int32_t* final_slot;
+    const int32_t* start_pos;
+    int export_grid;
+    float* export_states;
+    const int32_t* export_offsets;
+    int64_t export_capacity;
+    void* workspace;
+};
+
+// Upper bound on the number of 64-token chunks for num_seqs sequences holding
+// total_tokens tokens, whatever the split and start offsets.
+int64_t max_chunks(int num_seqs, int64_t total_tokens);
+size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_tokens);
+// stages: 1 = the UT transform (chunk table + T per chunk into the workspace),
+// 2 = the chunk scan (reads the workspace), 3 = both.
+constexpr int kStageTransform = 1;
+constexpr int kStageScan = 2;
+hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/gdn.h declares, sizes the workspace, and rejects bad host arguments with a
+clear message before anything is enqueued.
+
+Every call here is built to fail host validation: besides the argument under test,
+each one carries a second invalid argument that validation checks later (a NULL
+slot_out for decode, a zero workspace size for prefill), so no call can ever reach a
+kernel launch, on a machine with or without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_rule_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libgdn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == {"gdn_chunk_prefill_workspace_size", "gdn_recurrent_decode", "gdn_chunk_prefill",
+                          "gdn_chunk_prefill_transform", "gdn_chunk_prefill_scan", "gdn_mixed_step",
+                          "gdn_last_error"}
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.SIGNATURES) == set(names)
+
+
+def test_workspace_size():
+    lib = B.library()
+    s = B.make_shape(16, 32, 128, 128, B.GDN_BF16, 0.1)
+    n16 = lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s), 16, 16 * 8192)
+    chunks = (16 * 8192 + 63) // 64 + 2 * 16
+    assert n16 >= chunks * 32 * 64 * 64 * 4            # one fp32 T matrix per (chunk, head)
+    assert n16 % 256 == 0
+    s32 = B.make_shape(16, 32, 128, 128, B.GDN_F32, 0.1)
+    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s32), 16, 16 * 8192) == n16
+    bad = B.make_shape(3, 32, 128, 128, B.GDN_BF16, 0.1)
+    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(bad), 16, 1000) == 0
+    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s), 0, 0) > 0
+
+
+FAKE = 0x100000           # a 16-byte aligned stand-in address that is never dereferenced
+
+
+def _decode(shape=None, num_rows=4, q=FAKE, num_slots=8, slot_out=None):
+    lib = B.library()
+    shape = shape or B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
+    st = lib.gdn_recurrent_decode(ctypes.byref(shape), num_rows, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  num_slots, FAKE, slot_out, None)
+    return st, B.gdn_last_error()
+
+
+def _prefill(shape=None, num_seqs=2, total_tokens=100, export_grid=0, q=FAKE, cu=FAKE, ws_bytes=0,
+             num_export=0):
+    lib = B.library()
+    shape = shape or B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
+    st = lib.gdn_chunk_prefill(ctypes.byref(shape), num_seqs, total_tokens, cu, q, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, 8, FAKE, FAKE, None, export_grid, FAKE, FAKE, num_export, FAKE,
+                               ws_bytes, None)
+    return st, B.gdn_last_error()
+
+
+@pytest.mark.parametrize("shape,needle,code", [
+    (B.make_shape(3, 4, 64, 64, B.GDN_BF16, 0.1), "multiple of num_k_heads", B.GDN_ERR_UNSUPPORTED),
+    (B.make_shape(2, 4, 96, 64, B.GDN_BF16, 0.1), "64 or 128", B.GDN_ERR_UNSUPPORTED),
+    (B.make_shape(2, 4, 64, 256, B.GDN_BF16, 0.1), "64 or 128", B.GDN_ERR_UNSUPPORTED),
+    (B.make_shape(2, 4, 64, 64, 7, 0.1), "dtype 7", B.GDN_ERR_UNSUPPORTED),
+    (B.make_shape(0, 4, 64, 64, B.GDN_BF16, 0.1), "positive", B.GDN_ERR_INVALID_ARGUMENT),
+    (B.make_shape(2, 4, 64, 64, B.GDN_BF16, float("nan")), "scale", B.GDN_ERR_INVALID_ARGUMENT),
+])
+def test_bad_shapes(shape, needle, code):
+    for st, msg in (_decode(shape=shape), _prefill(shape=shape)):
+        assert st == code and needle in msg, (st, msg)
+
+
+def test_decode_validation():
+    st, msg = _decode(num_rows=-1)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_rows -1" in msg
+    st, msg = _decode(num_slots=-2)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_slots -2" in msg
+    st, msg = _decode(q=None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "q is NULL" in msg
+    st, msg = _decode(q=FAKE + 4)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "16-byte aligned" in msg
+    st, msg = _decode()
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "slot_out is NULL" in msg
+    # zero rows is a no-op, whatever the pointers
+    st, msg = _decode(num_rows=0, q=None)
+    assert st == B.GDN_OK and msg == ""
+
+
+def test_prefill_validation():
+    st, msg = _prefill(export_grid=1056)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "1056" in msg and "chunk size 64" in msg
+    st, msg = _prefill(export_grid=-64)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT
+    st, msg = _prefill(num_seqs=-1)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_seqs -1" in msg
+    st, msg = _prefill(total_tokens=-5)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "total_tokens -5" in msg
+    st, msg = _prefill(cu=None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "cu_seqlens is NULL" in msg
+    st, msg = _prefill(q=FAKE + 8)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "q (" in msg and "aligned" in msg
+    st, msg = _prefill(num_export=-1, export_grid=64)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_export_states" in msg
+    st, msg = _prefill(export_grid=1088)          # lcm(64, 1088) = 1088 is accepted; the workspace is not
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0" in msg
+    st, msg = _prefill()
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0 is smaller" in msg
+    st, msg = _prefill(num_seqs=0, q=None, cu=None)   # no sequences: a no-op
+    assert st == B.GDN_OK
+
+
+@pytest.mark.parametrize("entry", ["gdn_chunk_prefill_transform", "gdn_chunk_prefill_scan"])
+def test_prefill_stage_validation(entry):
+    fn = getattr(B.library(), entry)
+    shape = B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
+    st = fn(ctypes.byref(shape), 2, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None,
+            1056, FAKE, FAKE, 0, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "chunk size 64" in B.gdn_last_error()
+    st = fn(ctypes.byref(shape), 2, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None,
+            0, None, None, 0, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0" in B.gdn_last_error()
+
+
+def test_mixed_step_validation():
+    lib = B.library()
+    shape = B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
+    # decode part checked first: slot_out NULL
+    st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, None, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, 0, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "slot_out is NULL" in B.gdn_last_error()
+    # prefill part: export grid off the chunk grid
+    st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, 8, FAKE, FAKE, None, 100, FAKE, FAKE, 1, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_grid 100" in B.gdn_last_error()
+    # prefill part: workspace too small
+    st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, 0, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace" in B.gdn_last_error()
+
+
+def test_binding_checks_tensors_before_calling():
+    import torch
+    q = torch.zeros(2, 1, 64)
+    with pytest.raises(ValueError):
+        B.gdn_recurrent_decode(q, q, q, torch.zeros(2, 1), torch.zeros(2, 1), q, torch.zeros(1, 1, 64, 64),
+                               torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32), scale=1.0)
+    assert B.export_offsets([100, 64, 0, 1200], [0, 64, 5, 1000], 64) == [0, 1, 2, 2, 21]

@@ -138,24 +138,24 @@ struct Mma<__bf16> {
         for (int e = 0; e < 8; ++e) x[e] = row[nat(ks, g, e)] * scale[nat(ks, g, e)];
         return split(x);
     }
-    // B fragment (from-C order, step ks) out of 16-row accumulator tiles
-    static __device__ __forceinline__ frag acc_fromc(const f32x4* tiles, int ks) {
+    // B fragment (from-C order, step ks) out of 16-row accumulator tiles tiles[x * stride]
+    static __device__ __forceinline__ frag acc_fromc(const f32x4* tiles, int ks, int stride) {
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = tiles[2 * ks][i];
-            x[4 + i] = tiles[2 * ks + 1][i];
+            x[i] = tiles[(2 * ks) * stride][i];
+            x[4 + i] = tiles[(2 * ks + 1) * stride][i];
         }
         return round(x);
     }
     // the same, each row r scaled by scale[r] (or not, when scale is null), split
-    static __device__ __forceinline__ pair acc_fromc_split(const f32x4* tiles, int ks, int g,
+    static __device__ __forceinline__ pair acc_fromc_split(const f32x4* tiles, int ks, int stride, int g,
                                                            const float* scale) {
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = tiles[2 * ks][i];
-            x[4 + i] = tiles[2 * ks + 1][i];
+            x[i] = tiles[(2 * ks) * stride][i];
+            x[4 + i] = tiles[(2 * ks + 1) * stride][i];
             if (scale) {
                 x[i] *= scale[32 * ks + 4 * g + i];
                 x[4 + i] *= scale[32 * ks + 16 + 4 * g + i];
@@ -190,10 +190,12 @@ struct Mma<float> {
                                                                 const float* scale) {
         return pair{row[nat(ks, g, 0)] * scale[nat(ks, g, 0)]};
     }
-    static __device__ __forceinline__ frag acc_fromc(const f32x4* tiles, int ks) { return tiles[ks >> 2][ks & 3]; }
-    static __device__ __forceinline__ pair acc_fromc_split(const f32x4* tiles, int ks, int g,
+    static __device__ __forceinline__ frag acc_fromc(const f32x4* tiles, int ks, int stride) {
+        return tiles[(ks >> 2) * stride][ks & 3];
+    }
+    static __device__ __forceinline__ pair acc_fromc_split(const f32x4* tiles, int ks, int stride, int g,
                                                            const float* scale) {
-        float x = tiles[ks >> 2][ks & 3];
+        float x = tiles[(ks >> 2) * stride][ks & 3];
         if (scale) x *= scale[fromc(ks, g, 0)];
         return pair{x};
     }
@@ -214,14 +216,6 @@ __device__ __forceinline__ void copy16(void* dst, const void* src) {
 }
 __device__ __forceinline__ void zero16(void* dst) {
     *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
-}
-
-// In-chunk inclusive cumulative sum of g, computed left to right, identically in
-// every kernel that needs it.  gl[s] holds g (0 past the chunk's end).
-__device__ __forceinline__ float chunk_cumsum(const float* gl, int r) {
-    float acc = 0.f;
-    for (int s = 0; s <= r; ++s) acc += gl[s];
-    return acc;
 }
 
 // ---------------------------------------------------------------- prep kernel
@@ -282,19 +276,40 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t* cu, const int3
     if (tid == 0) seq_off[N] = carry;
 }
 
-// ---------------------------------------------------------------- T = (I + A)^-1
+// ---------------------------------------------------------------- gates and T = (I + A)^-1
 
+// Per (chunk, value head) gate vectors written by the transform and read by the scan.
+constexpr int kGates = 5;
+enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_BG = 3, GATE_KDEC = 4 };
+
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele, fixed order).
+__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// One wave per (chunk, value head).  Writes the chunk's gate vectors (G, e^G, beta,
+// beta e^G, e^(G_last - G)) and T = (I + A)^-1 in fp32.  T is formed blockwise: the
+// four 16x16 diagonal blocks by forward substitution (lane 16b + j owns column j of
+// block b), then the off-diagonal blocks column block by column block,
+//     T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj,
+// on fp32 MFMA, each T_ij overwriting A_ij (whose last use it is).
 template <typename E, int DK>
 __global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* table,
-                                                     const int32_t* seq_off, int nc_max, float* tws) {
+                                                     const int32_t* seq_off, int nc_max, float* tws,
+                                                     float* gws) {
     using M = Mma<E>;
     constexpr int KLD = DK + Pad<E>::value;
     constexpr int ALD = kC + 4;
     constexpr int KBYTES = kC * KLD * (int)sizeof(E);
     constexpr int ABYTES = kC * ALD * (int)sizeof(float);
-    // one buffer holds K while K K^T is formed, then A, then T for the store
+    // one buffer holds K while K K^T is formed, then A, then T (in place)
     __shared__ __attribute__((aligned(16))) char buf[KBYTES > ABYTES ? KBYTES : ABYTES];
-    __shared__ float gl[kC], Gs[kC], bl[kC];
+    __shared__ float Gs[kC], bl[kC];
     E* ks = reinterpret_cast<E*>(buf);
     float* as = reinterpret_cast<float*>(buf);
 
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* t
     const int li = lane & 15, g4 = lane >> 4;
 
     // K rows of the chunk -> LDS (zero past L)
-    constexpr int VPR = DK / Vec<E>::N;   // 16-byte vectors per row
+    constexpr int VPR = DK / Vec<E>::N;
     const E* kg = static_cast<const E*>(a.k);
     for (int idx = lane; idx < kC * VPR; idx += 64) {
         const int r = idx / VPR, vi = idx - r * VPR;
@@ -317,10 +332,21 @@ __global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* t
         if (r < L) copy16(dst, kg + ((size_t)(tok + r) * a.H_k + kh) * DK + vi * Vec<E>::N);
         else zero16(dst);
     }
-    gl[lane] = lane < L ? a.g[(size_t)(tok + lane) * a.H_v + h] : 0.f;
-    bl[lane] = lane < L ? a.beta[(size_t)(tok + lane) * a.H_v + h] : 0.f;
+    // gates: lane s holds token s (g = beta = 0 past L, so G is flat there)
+    const float gs = lane < L ? a.g[(size_t)(tok + lane) * a.H_v + h] : 0.f;
+    const float bs = lane < L ? a.beta[(size_t)(tok + lane) * a.H_v + h] : 0.f;
+    const float G = wave_inclusive_sum(gs, lane);
+    const float G_last = __shfl(G, kC - 1, 64);
+    const float gam = expf(G);
+    float* gout = gws + ((size_t)c * a.H_v + h) * (kGates * kC);
+    gout[GATE_G * kC + lane] = G;
+    gout[GATE_GAM * kC + lane] = gam;
+    gout[GATE_BET * kC + lane] = bs;
+    gout[GATE_BG * kC + lane] = bs * gam;
+    gout[GATE_KDEC * kC + lane] = expf(G_last - G);
+    Gs[lane] = G;
+    bl[lane] = bs;
     __syncthreads();
-    Gs[lane] = chunk_cumsum(gl, lane);
 
     // K K^T for the 10 lower 16x16 tiles, kept in registers (products of exact inputs)
     f32x4 kk_t[10];
@@ -355,29 +381,51 @@ __global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* t
     }
     __syncthreads();
 
-    // forward substitution, lane j owns column j of T (T[r][j] = 0 for r < j, 1 at r == j);
-    // the dot over s is split into four interleaved partial sums, added in a fixed order
-    const int j = lane;
-    float t[kC];
+    // diagonal blocks: lane (b, j) forms column j of (I + A_bb)^-1
+    {
+        const int b = g4, j = li;
+        const float* Ab = as + (16 * b) * ALD + 16 * b;
+        float t[16];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
 #pragma unroll
-        for (int s = 0; s < r; ++s) {
-            const float x = -as[r * ALD + s] * t[s];
-            if ((s & 3) == 0) p0 += x;
-            else if ((s & 3) == 1) p1 += x;
-            else if ((s & 3) == 2) p2 += x;
-            else p3 += x;
+            for (int s = 0; s < r; ++s) acc = fmaf(-Ab[r * ALD + s], t[s], acc);
+            t[r] = r < j ? 0.f : (r == j ? 1.f : acc);
         }
-        const float acc = (p0 + p1) + (p2 + p3);
-        t[r] = r < j ? 0.f : (r == j ? 1.f : acc);
+        __syncthreads();
+        float* Tb = as + (16 * b) * ALD + 16 * b;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Tb[r * ALD + j] = t[r];
     }
     __syncthreads();
-    // transpose through LDS and store T rows contiguously
+
+    // off-diagonal blocks on fp32 MFMA (16x16x4): X = sum_k A_ik T_kj, then T_ij = -T_ii X
 #pragma unroll
-    for (int r = 0; r < kC; ++r) as[r * ALD + j] = t[r];
-    __syncthreads();
+    for (int jb = 0; jb < 3; ++jb) {
+#pragma unroll
+        for (int ib = jb + 1; ib < 4; ++ib) {
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = jb; kb < ib; ++kb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    X = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        as[(16 * ib + li) * ALD + 16 * kb + 4 * q + g4],     // A_ik[m][4q + g]
+                        as[(16 * kb + 4 * q + g4) * ALD + 16 * jb + li],     // T_kj[4q + g][n]
+                        X, 0, 0, 0);
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)   // B from X's registers: element q is row 4g + q
+                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(as[(16 * ib + li) * ALD + 16 * ib + 4 * g4 + q], X[q],
+                                                         Y, 0, 0, 0);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) as[(16 * ib + 4 * g4 + i) * ALD + 16 * jb + li] = -Y[i];
+            __syncthreads();
+        }
+    }
+
     float* out = tws + ((size_t)c * a.H_v + h) * (kC * kC);
     for (int idx = lane; idx < kC * kC / 4; idx += 64) {
         const int r = idx >> 4, s4 = (idx & 15) * 4;
@@ -389,38 +437,41 @@ __global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* t
 
 template <typename E, int DK, int DV>
 struct ChainSmem {
-    static constexpr int KLD = DK + Pad<E>::value;
-    static constexpr int VLD = DV + Pad<E>::value;
-    static constexpr int TLD = kC + 4;                  // fp32 T
-    static constexpr int PLD = kC + Pad<E>::value;      // P in the operand type
-    E k[kC * KLD];
-    E q[kC * KLD];
-    E w[kC * KLD];        // -W
-    E v[kC * VLD];
+    static constexpr int QLD = DK + Pad<E>::value;      // Q rows
+    static constexpr int TTLD = kC + Pad<E>::value;     // K^T rows (one per d_k index, tokens along)
+    static constexpr int VLD = DV + Pad<E>::value;      // V rows
+    static constexpr int WLD = DK + Pad<E>::value;      // -W rows
+    static constexpr int TLD = kC + 4;                  // fp32 T rows
+    static constexpr int PLD = kC + Pad<E>::value;      // P rows
+    E q[kC * QLD];
+    E kt[DK * TTLD];
     union {
-        float t[kC * TLD];    // T (phase A)
-        E p[kC * PLD];        // P (phases B-D)
+        E v[kC * VLD];    // V (until U~ is formed)
+        E w[kC * WLD];    // then -W
     };
-    float gl[kC];       // g (0 past the end)
-    float G[kC];        // in-chunk cumulative log decay
-    float gam[kC];      // e^G
-    float bet[kC];      // beta
-    float bg[kC];       // beta e^G
-    float kdec[kC];     // e^(G_last - G)
+    float t[kC * TLD];
+    E p[kC * PLD];
+    float gate[kGates * kC];
 };
 
+// smallest k index that step ks of each order covers
+template <typename M>
+__device__ __forceinline__ int kmin_nat(int ks) { return ks * M::KSTEP; }
+template <typename M>
+__device__ __forceinline__ int kmin_fromc(int ks) { return M::KSTEP == 32 ? 32 * ks : 16 * (ks >> 2); }
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4* table,
-                                                        const int32_t* seq_off, int nc_max,
-                                                        const float* tws) {
+__global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int nc_max, const float* tws,
+                  const float* gws) {
     using M = Mma<E>;
     using S = ChainSmem<E, DK, DV>;
     constexpr int NW = DV / 32;            // waves; wave w owns columns [32w, 32w + 32)
+    constexpr int NT = NW * 64;            // threads
     constexpr int MT_S = DK / 16;          // 16-row tiles of the state
     constexpr int KS_DK = DK / M::KSTEP;   // k steps over d_k
     constexpr int KS_C = kC / M::KSTEP;    // k steps over the chunk
-    constexpr int VPRK = DK / Vec<E>::N;
-    constexpr int VPRV = DV / Vec<E>::N;
+    constexpr int VN = Vec<E>::N;
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int seq = blockIdx.x / a.H_v;
@@ -431,6 +482,11 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
     const int lane = tid & 63;
     const int li = lane & 15, g4 = lane >> 4;
     const int col0 = 32 * wv;
+    const float* bet = sm.gate + GATE_BET * kC;
+    const float* bg = sm.gate + GATE_BG * kC;
+    const float* gam = sm.gate + GATE_GAM * kC;
+    const float* Gv = sm.gate + GATE_G * kC;
+    const float* kdec = sm.gate + GATE_KDEC * kC;
 
     const size_t SE = (size_t)DK * DV;
     // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
@@ -467,48 +523,48 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
     for (int c = c_begin; c < c_end; ++c) {
         const int4 ent = table[c];
         const int tok = ent.y, L = ent.z;
-        __syncthreads();   // previous chunk is done with LDS
+        __syncthreads();   // the previous chunk is done with LDS
 
-        // ---- loads: K, Q, V rows, T, gates
-        for (int idx = tid; idx < kC * VPRK; idx += NW * 64) {
-            const int r = idx / VPRK, vi = idx - r * VPRK;
-            E* dk_ = sm.k + r * S::KLD + vi * Vec<E>::N;
-            E* dq_ = sm.q + r * S::KLD + vi * Vec<E>::N;
+        // ---- loads: Q rows, K transposed, V rows, T, gates
+        for (int idx = tid; idx < kC * (DK / VN); idx += NT) {
+            const int r = idx / (DK / VN), d0 = (idx - r * (DK / VN)) * VN;
+            E* dq = sm.q + r * S::QLD + d0;
+            if (r < L) copy16(dq, qg + ((size_t)(tok + r) * a.H_k + kh) * DK + d0);
+            else zero16(dq);
+        }
+        // K: consecutive threads take consecutive tokens, so the transposed LDS writes
+        // of a wave fall in consecutive addresses
+        for (int idx = tid; idx < kC * (DK / VN); idx += NT) {
+            const int r = idx & (kC - 1), d0 = (idx >> 6) * VN;
+            E kv[VN];
             if (r < L) {
-                const size_t off = ((size_t)(tok + r) * a.H_k + kh) * DK + vi * Vec<E>::N;
-                copy16(dk_, kg + off);
-                copy16(dq_, qg + off);
+                *reinterpret_cast<uint4*>(kv) =
+                    *reinterpret_cast<const uint4*>(kg + ((size_t)(tok + r) * a.H_k + kh) * DK + d0);
             } else {
-                zero16(dk_);
-                zero16(dq_);
+                *reinterpret_cast<uint4*>(kv) = make_uint4(0u, 0u, 0u, 0u);
             }
+#pragma unroll
+            for (int e = 0; e < VN; ++e) sm.kt[(d0 + e) * S::TTLD + r] = kv[e];
         }
-        for (int idx = tid; idx < kC * VPRV; idx += NW * 64) {
-            const int r = idx / VPRV, vi = idx - r * VPRV;
-            E* dv_ = sm.v + r * S::VLD + vi * Vec<E>::N;
-            if (r < L) copy16(dv_, vg + ((size_t)(tok + r) * a.H_v + h) * DV + vi * Vec<E>::N);
-            else zero16(dv_);
+        for (int idx = tid; idx < kC * (DV / VN); idx += NT) {
+            const int r = idx / (DV / VN), vi = idx - r * (DV / VN);
+            E* dv = sm.v + r * S::VLD + vi * VN;
+            if (r < L) copy16(dv, vg + ((size_t)(tok + r) * a.H_v + h) * DV + vi * VN);
+            else zero16(dv);
         }
-        const float* tsrc = tws + ((size_t)c * a.H_v + h) * (kC * kC);
-        for (int idx = tid; idx < kC * kC / 4; idx += NW * 64) {
-            const int r = idx >> 4, s4 = (idx & 15) * 4;
-            copy16(sm.t + r * S::TLD + s4, tsrc + r * kC + s4);
-        }
-        if (tid < kC) {
-            sm.gl[tid] = tid < L ? a.g[(size_t)(tok + tid) * a.H_v + h] : 0.f;
-            sm.bet[tid] = tid < L ? a.beta[(size_t)(tok + tid) * a.H_v + h] : 0.f;
-        }
-        __syncthreads();
-        if (tid < kC) {
-            const float Gr = chunk_cumsum(sm.gl, tid);
-            sm.G[tid] = Gr;
-            sm.gam[tid] = expf(Gr);
-            sm.bg[tid] = sm.bet[tid] * expf(Gr);
+        {
+            const float* tsrc = tws + ((size_t)c * a.H_v + h) * (kC * kC);
+            for (int idx = tid; idx < kC * kC / 4; idx += NT) {
+                const int r = idx >> 4, s4 = (idx & 15) * 4;
+                copy16(sm.t + r * S::TLD + s4, tsrc + r * kC + s4);
+            }
+            const float* gsrc = gws + ((size_t)c * a.H_v + h) * (kGates * kC);
+            for (int idx = tid; idx < kGates * kC / 4; idx += NT) copy16(sm.gate + 4 * idx, gsrc + 4 * idx);
         }
         __syncthreads();
-        if (tid < kC) sm.kdec[tid] = expf(sm.G[kC - 1] - sm.G[tid]);   // G[63] = G_last
 
-        // ---- phase A: U~ = (T diag(beta)) V (strip, registers); -W = -(T diag(beta gamma)) K (LDS)
+        // ---- phase A1: U~ = (T diag(beta)) V for this wave's strip (T is lower triangular:
+        //      steps wholly above the diagonal are skipped)
         f32x4 Uacc[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -516,40 +572,44 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
             Uacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
-                const typename M::pair ta = M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, sm.bet);
+                if (kmin_nat<M>(kk) > 16 * mt + 15) continue;
+                const typename M::pair ta = M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, bet);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     Uacc[mt][nt] = M::mma_sa(ta, M::col_nat(sm.v, S::VLD, col0 + 16 * nt + li, kk, g4),
                                              Uacc[mt][nt]);
             }
         }
+        __syncthreads();   // V is dead: its space takes -W
+
+        // ---- phase A2 + B (shared, split over the waves):
+        //      -W = -(T diag(beta gamma)) K  and  P = (Q K^T) o D o lower-incl-diagonal
         for (int t = wv; t < 4 * (DK / 16); t += NW) {
             const int mt = t / (DK / 16), nt = t - mt * (DK / 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KS_C; ++kk)
-                acc = M::mma_sa(M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, sm.bg),
-                                M::col_nat(sm.k, S::KLD, 16 * nt + li, kk, g4), acc);
+            for (int kk = 0; kk < KS_C; ++kk) {
+                if (kmin_nat<M>(kk) > 16 * mt + 15) continue;
+                acc = M::mma_sa(M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, bg),
+                                M::row_nat(sm.kt + (16 * nt + li) * S::TTLD, kk, g4), acc);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sm.w[(16 * mt + 4 * g4 + i) * S::KLD + 16 * nt + li] = (E)(-acc[i]);
+                sm.w[(16 * mt + 4 * g4 + i) * S::WLD + 16 * nt + li] = (E)(-acc[i]);
         }
-        __syncthreads();
-
-        // ---- phase B: P = (Q K^T) o D o lower-incl-diagonal -> LDS (over T)
         for (int t = wv; t < 16; t += NW) {
             const int mt = t >> 2, nt = t & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (nt <= mt) {
 #pragma unroll 4
                 for (int kk = 0; kk < KS_DK; ++kk)
-                    acc = M::mma(M::row_nat(sm.q + (16 * mt + li) * S::KLD, kk, g4),
-                                 M::row_nat(sm.k + (16 * nt + li) * S::KLD, kk, g4), acc);
+                    acc = M::mma(M::row_nat(sm.q + (16 * mt + li) * S::QLD, kk, g4),
+                                 M::col_nat(sm.kt, S::TTLD, 16 * nt + li, kk, g4), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                const float val = s <= r ? acc[i] * expf(sm.G[r] - sm.G[s]) : 0.f;
+                const float val = s <= r ? acc[i] * expf(Gv[r] - Gv[s]) : 0.f;
                 sm.p[r * S::PLD + s] = (E)val;
             }
         }
@@ -557,48 +617,42 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
 
         // ---- phase C: U = U~ + (-W) S
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 col[MT_S];
+        for (int kk = 0; kk < KS_DK; ++kk) {
+            const typename M::frag sb0 = M::acc_fromc(&Sacc[0][0], kk, 2);
+            const typename M::frag sb1 = M::acc_fromc(&Sacc[0][1], kk, 2);
 #pragma unroll
-            for (int x = 0; x < MT_S; ++x) col[x] = Sacc[x][nt];
-#pragma unroll
-            for (int kk = 0; kk < KS_DK; ++kk) {
-                const typename M::frag sb = M::acc_fromc(col, kk);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    Uacc[mt][nt] = M::mma(M::row_fromc(sm.w + (16 * mt + li) * S::KLD, kk, g4), sb, Uacc[mt][nt]);
+            for (int mt = 0; mt < 4; ++mt) {
+                const typename M::frag wa = M::row_fromc(sm.w + (16 * mt + li) * S::WLD, kk, g4);
+                Uacc[mt][0] = M::mma(wa, sb0, Uacc[mt][0]);
+                Uacc[mt][1] = M::mma(wa, sb1, Uacc[mt][1]);
             }
         }
 
-        // ---- phase D: O = gamma o (Q S) + P U
+        // ---- phase D: O = gamma o (Q S) + P U, one 16-column tile at a time
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            f32x4 col[MT_S];
-#pragma unroll
-            for (int x = 0; x < MT_S; ++x) col[x] = Sacc[x][nt];
-            f32x4 ucol[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) ucol[x] = Uacc[x][nt];
             f32x4 Oacc[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk) {
-                const typename M::frag sb = M::acc_fromc(col, kk);
+                const typename M::frag sb = M::acc_fromc(&Sacc[0][nt], kk, 2);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
-                    Oacc[mt] = M::mma(M::row_fromc(sm.q + (16 * mt + li) * S::KLD, kk, g4), sb, Oacc[mt]);
+                    Oacc[mt] = M::mma(M::row_fromc(sm.q + (16 * mt + li) * S::QLD, kk, g4), sb, Oacc[mt]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Oacc[mt][i] *= sm.gam[16 * mt + 4 * g4 + i];
+                for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gam[16 * mt + 4 * g4 + i];
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
-                const typename M::pair ub = M::acc_fromc_split(ucol, kk, g4, nullptr);
+                const typename M::pair ub = M::acc_fromc_split(&Uacc[0][nt], kk, 2, g4, nullptr);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (kmin_fromc<M>(kk) > 16 * mt + 15) continue;
                     Oacc[mt] = M::mma_sb(M::row_fromc(sm.p + (16 * mt + li) * S::PLD, kk, g4), ub, Oacc[mt]);
+                }
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -611,22 +665,23 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
         }
 
         // ---- phase E: S = gamma_last S + K^T (diag(e^(G_last - G)) U)
-        const float gl_last = sm.gam[kC - 1];
+        const float gl_last = gam[kC - 1];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 ucol[4];
+        for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) ucol[x] = Uacc[x][nt];
+            for (int i = 0; i < 4; ++i) {
+                Sacc[mt][0][i] *= gl_last;
+                Sacc[mt][1][i] *= gl_last;
+            }
 #pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt)
+        for (int kk = 0; kk < KS_C; ++kk) {
+            const typename M::pair ub0 = M::acc_fromc_split(&Uacc[0][0], kk, 2, g4, kdec);
+            const typename M::pair ub1 = M::acc_fromc_split(&Uacc[0][1], kk, 2, g4, kdec);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Sacc[mt][nt][i] *= gl_last;
-#pragma unroll
-            for (int kk = 0; kk < KS_C; ++kk) {
-                const typename M::pair ub = M::acc_fromc_split(ucol, kk, g4, sm.kdec);
-#pragma unroll
-                for (int mt = 0; mt < MT_S; ++mt)
-                    Sacc[mt][nt] = M::mma_sb(M::col_fromc(sm.k, S::KLD, 16 * mt + li, kk, g4), ub, Sacc[mt][nt]);
+            for (int mt = 0; mt < MT_S; ++mt) {
+                const typename M::frag ka = M::row_fromc(sm.kt + (16 * mt + li) * S::TTLD, kk, g4);
+                Sacc[mt][0] = M::mma_sb(ka, ub0, Sacc[mt][0]);
+                Sacc[mt][1] = M::mma_sb(ka, ub1, Sacc[mt][1]);
             }
         }
 
@@ -666,7 +721,7 @@ __global__ __launch_bounds__(DV * 2) void chain_kernel(PrefillArgs a, const int4
 // ---------------------------------------------------------------- workspace layout
 
 struct Layout {
-    size_t table, seq_off, tws, total;
+    size_t table, seq_off, tws, gws, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -677,7 +732,8 @@ Layout layout(int H_v, int num_seqs, int64_t total_tokens) {
     l.table = 0;
     l.seq_off = align256(l.table + (size_t)nc * sizeof(int4));
     l.tws = align256(l.seq_off + (size_t)(num_seqs + 1) * sizeof(int32_t));
-    l.total = align256(l.tws + (size_t)nc * H_v * kC * kC * sizeof(float));
+    l.gws = align256(l.tws + (size_t)nc * H_v * kC * kC * sizeof(float));
+    l.total = align256(l.gws + (size_t)nc * H_v * kGates * kC * sizeof(float));
     return l;
 }
 
@@ -689,6 +745,7 @@ hipError_t launch_typed(const PrefillArgs& a, int stages, hipStream_t stream) {
     int4* table = reinterpret_cast<int4*>(ws + l.table);
     int32_t* seq_off = reinterpret_cast<int32_t*>(ws + l.seq_off);
     float* tws = reinterpret_cast<float*>(ws + l.tws);
+    float* gws = reinterpret_cast<float*>(ws + l.gws);
     const int nc_max = (int)max_chunks(a.num_seqs, a.total_tokens);
 
     if (stages & 1) {
@@ -697,13 +754,13 @@ hipError_t launch_typed(const PrefillArgs& a, int stages, hipStream_t stream) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((tsolve_kernel<E, DK>), dim3(nc_max, a.H_v), dim3(64), 0, stream, a, table,
-                           seq_off, nc_max, tws);
+                           seq_off, nc_max, tws, gws);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     if (stages & 2) {
         hipLaunchKernelGGL((chain_kernel<E, DK, DV>), dim3(a.num_seqs * a.H_v), dim3(DV * 2), 0, stream,
-                           a, table, seq_off, nc_max, tws);
+                           a, table, seq_off, nc_max, tws, gws);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -5,10 +5,10 @@ One step is one pass of the whole path over one batch: a mixed step whose front 
 the standard decode batch (64 cached rows, 16 key / 32 value heads, d_k = d_v = 128,
 bf16 q/k/v, fp32 states in a 256-slot cache) and whose prefill part is the long
 prefill (16 sequences x 8192 tokens, same heads, zero initial states, states exported
-on the 1088-token prefix-cache grid).  The step is issued as its three stages --
-gdn_recurrent_decode, gdn_chunk_prefill_transform, gdn_chunk_prefill_scan -- which is
+on the 1088-token prefix-cache grid).  The step is issued as its two launches --
+gdn_recurrent_decode (one kernel) then gdn_chunk_prefill (one kernel) -- which is
 exactly what gdn_mixed_step enqueues (checked bitwise before timing), so that HIP
-events on the launch stream time each stage.  Inputs are resident in HBM before the
+events on the launch stream time each kernel.  Inputs are resident in HBM before the
 timed region starts.
 
 Prints one JSON line: value = prefill tokens per second of the whole step; the
@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4,
                     help="prefill sequences (of 16) the oracle runs for the CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB, a reference "
+                         "dispatch of known traffic for hardware byte counters")
     return ap.parse_args()
 
 
@@ -67,6 +70,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18                # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_gen = time.time()
     wd = W.config(1)                                           # decode batch
     wp = W.config(4, fill_pool=False)                          # long prefill
@@ -107,11 +118,8 @@ def main():
     def stage_decode():
         binding.gdn_recurrent_decode(dq, dk_, dv_, dg, db, do, pool, slot_in, slot_out, scale=wd.scale)
 
-    def stage_transform():
-        binding.gdn_chunk_prefill_transform(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
-
-    def stage_scan():
-        binding.gdn_chunk_prefill_scan(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
+    def stage_prefill():
+        binding.gdn_chunk_prefill(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
 
     # the staged step is the mixed step: check bitwise once, from the same pool
     pool0 = pool.clone()
@@ -119,7 +127,7 @@ def main():
     torch.cuda.synchronize()
     ref = (o.clone(), pool.clone(), exports.clone())
     pool.copy_(pool0)
-    stage_decode(); stage_transform(); stage_scan()
+    stage_decode(); stage_prefill()
     torch.cuda.synchronize()
     same = torch.equal(o, ref[0]) and torch.equal(pool, ref[1]) and torch.equal(exports, ref[2])
     if not same:
@@ -128,11 +136,11 @@ def main():
     del pool0, ref
 
     for _ in range(args.warmup):
-        stage_decode(); stage_transform(); stage_scan()
+        stage_decode(); stage_prefill()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -140,41 +148,34 @@ def main():
         ev[i][0].record()
         stage_decode()
         ev[i][1].record()
-        stage_transform()
+        stage_prefill()
         ev[i][2].record()
-        stage_scan()
-        ev[i][3].record()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
     t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    t_tr = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    t_scan = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    t_pre = sum(e[1].elapsed_time(e[2]) for e in ev) / K
 
     # ---- figures
     value = Tp / (ms_step * 1e-3)
     dec_bytes = 2 * 4 * d_k * d_v * B * H_v                # fp32 state read + write per (row, head)
     dec_gbps = dec_bytes / (t_dec * 1e-3) / 1e9
     f_tok = algorithmic_flops_per_token(H_k, H_v, d_k, d_v)
-    kkt_tok = H_k * CHUNK * d_k                            # K K^T lower half, in the transform stage
-    scan_flops = (f_tok - kkt_tok) * Tp
-    scan_tflops = scan_flops / (t_scan * 1e-3) / 1e12
-    prefill_ms = t_tr + t_scan
+    pre_flops = f_tok * Tp
+    pre_tflops = pre_flops / (t_pre * 1e-3) / 1e12
     kernels = {
-        "decode": {"ms": round(t_dec, 5), "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                   "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": dec_bytes},
-        "prefill_scan": {"ms": round(t_scan, 4), "bound": "mfma", "achieved": round(scan_tflops, 2),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / BF16_PEAK_TFLOPS, 4),
-                         "flops_per_launch": scan_flops},
-        "prefill_transform": {"ms": round(t_tr, 4)},
+        "decode_kernel": {"ms": round(t_dec, 5), "bound": "hbm", "achieved": round(dec_gbps, 1),
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_launch": dec_bytes},
+        "scan_kernel": {"ms": round(t_pre, 4), "bound": "mfma", "achieved": round(pre_tflops, 2),
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                        "flops_per_launch": pre_flops},
     }
-    dominant = max(("decode", t_dec), ("prefill_scan", t_scan), ("prefill_transform", t_tr), key=lambda x: x[1])[0]
-    roof = kernels["prefill_scan"] if dominant != "decode" else kernels["decode"]
-    roofline = {"kernel": "chain_kernel (gdn_chunk_prefill_scan)" if roof is kernels["prefill_scan"]
-                else "decode_kernel (gdn_recurrent_decode)",
-                "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"], "unit": roof["unit"],
-                "frac": roof["frac"], "traffic": None}
+    dominant = "scan_kernel" if t_pre >= t_dec else "decode_kernel"
+    roof = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"],
+                "unit": roof["unit"], "frac": roof["frac"], "traffic": None}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -187,17 +188,16 @@ def main():
                    "parallelism": "single GPU"},
         "decode": {"state_GB_per_s": round(dec_gbps, 1), "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "ms": round(t_dec, 5), "state_bytes": dec_bytes},
-        "prefill": {"tokens_per_s": round(Tp / (prefill_ms * 1e-3), 1), "ms": round(prefill_ms, 4),
-                    "mfma_frac": round(f_tok * Tp / (prefill_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "flops_per_token": f_tok},
+        "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": round(t_pre, 4),
+                    "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok},
         "roofline": roofline,
         "kernels": kernels,
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp, wd, args.cpu_sample_seqs)
-    print("input generation %.1f s; step %.3f ms = decode %.4f + transform %.4f + scan %.4f ms" % (
-        gen_s, ms_step, t_dec, t_tr, t_scan), file=sys.stderr)
+    print("input generation %.1f s; step %.3f ms = decode %.4f + prefill %.4f ms" % (
+        gen_s, ms_step, t_dec, t_pre), file=sys.stderr)
     print(json.dumps(out), flush=True)
 
 

@@ -47,12 +47,6 @@ SIGNATURES = {
     "gdn_chunk_prefill": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _sz,
                                          _vp]),
-    "gdn_chunk_prefill_transform": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _i64, _vp, _vp, _vp, _vp, _vp,
-                                                   _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp,
-                                                   _sz, _vp]),
-    "gdn_chunk_prefill_scan": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
-                                              _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _sz,
-                                              _vp]),
     "gdn_mixed_step": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64,
                                       _vp, _sz, _vp]),
@@ -229,22 +223,6 @@ def gdn_chunk_prefill(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, fi
                   scale, workspace, start_pos, export_grid, export_states, export_offsets, stream)
 
 
-def gdn_chunk_prefill_transform(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot, *,
-                                scale: float, workspace, start_pos=None, export_grid: int = 0,
-                                export_states=None, export_offsets=None, stream=None) -> None:
-    """First stage of gdn_chunk_prefill: chunk table and UT transform into the workspace."""
-    _prefill_call("gdn_chunk_prefill_transform", q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot,
-                  final_slot, scale, workspace, start_pos, export_grid, export_states, export_offsets, stream)
-
-
-def gdn_chunk_prefill_scan(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot, *,
-                           scale: float, workspace, start_pos=None, export_grid: int = 0,
-                           export_states=None, export_offsets=None, stream=None) -> None:
-    """Second stage of gdn_chunk_prefill: the sequential chunk scan from the workspace."""
-    _prefill_call("gdn_chunk_prefill_scan", q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot,
-                  final_slot, scale, workspace, start_pos, export_grid, export_states, export_offsets, stream)
-
-
 def gdn_mixed_step(q, k, v, g, beta, o, state_pool, slot_in, slot_out, cu_seqlens_prefill, init_slot,
                    final_slot, *, scale: float, workspace, start_pos=None, export_grid: int = 0,
                    export_states=None, export_offsets=None, stream=None) -> None:
@@ -268,7 +246,8 @@ def gdn_mixed_step(q, k, v, g, beta, o, state_pool, slot_in, slot_out, cu_seqlen
 
 
 def alloc_workspace(H_v: int, dtype: torch.dtype, num_seqs: int, total_tokens: int, device) -> torch.Tensor:
-    """A uint8 device buffer of the size gdn_chunk_prefill needs (torch allocates it)."""
+    """A uint8 device buffer of the size gdn_chunk_prefill needs (torch allocates it;
+    at least 256 bytes so that it always has a valid address)."""
     code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
     n = gdn_chunk_prefill_workspace_size(1, H_v, 64, 64, code, num_seqs, total_tokens)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

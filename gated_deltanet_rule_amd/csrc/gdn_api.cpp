@@ -110,12 +110,11 @@ gdn_status check_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total
         return fail(GDN_ERR_INVALID_ARGUMENT, "num_export_states %lld is negative",
                     (long long)num_export_states);
     if (num_seqs == 0) return GDN_OK;
-    if (gdn::max_chunks(num_seqs, total_tokens) * shape->num_v_heads > 0x7fffffffLL ||
-        (int64_t)num_seqs * shape->num_v_heads > 0x7fffffffLL)
+    if ((int64_t)num_seqs * shape->num_v_heads > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "problem too large for one launch (num_seqs %d, total_tokens %lld)",
                     num_seqs, (long long)total_tokens);
     st = check_ptrs({{"cu_seqlens", cu_seqlens, 4}, {"init_slot", init_slot, 4},
-                     {"final_slot", final_slot, 4}, {"workspace", workspace, 256}});
+                     {"final_slot", final_slot, 4}});
     if (st != GDN_OK) return st;
     if (start_pos && !aligned(start_pos, 4))
         return fail(GDN_ERR_INVALID_ARGUMENT, "start_pos is not 4-byte aligned");
@@ -140,6 +139,10 @@ gdn_status check_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total
     if (workspace_bytes < need)
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace_bytes %zu is smaller than the %zu bytes required",
                     workspace_bytes, need);
+    if (need > 0) {
+        st = check_ptrs({{"workspace", workspace, 256}});
+        if (st != GDN_OK) return st;
+    }
     return GDN_OK;
 }
 
@@ -226,15 +229,13 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows, const 
                       "decode launch");
 }
 
-namespace {
-
-gdn_status prefill_entry(int stages, const char* what, const gdn_shape* shape, int32_t num_seqs,
-                         int64_t total_tokens, const int32_t* cu_seqlens, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, void* o, float* state_pool,
-                         int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
-                         const int32_t* start_pos, int32_t export_grid, float* export_states,
-                         const int32_t* export_offsets, int64_t num_export_states, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
+                             const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, void* o, float* state_pool,
+                             int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
+                             const int32_t* start_pos, int32_t export_grid, float* export_states,
+                             const int32_t* export_offsets, int64_t num_export_states, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
     g_last_error.clear();
     gdn_status st = check_prefill(shape, num_seqs, total_tokens, cu_seqlens, q, k, v, g, beta, o,
                                   state_pool, num_slots, init_slot, final_slot, start_pos, export_grid,
@@ -245,48 +246,8 @@ gdn_status prefill_entry(int stages, const char* what, const gdn_shape* shape, i
                                                        g, beta, o, state_pool, num_slots, init_slot,
                                                        final_slot, start_pos, export_grid, export_states,
                                                        export_offsets, num_export_states, workspace),
-                                          stages, stream),
-                      what);
-}
-
-}  // namespace
-
-gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
-                             const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
-                             const float* g, const float* beta, void* o, float* state_pool,
-                             int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
-                             const int32_t* start_pos, int32_t export_grid, float* export_states,
-                             const int32_t* export_offsets, int64_t num_export_states, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-    return prefill_entry(gdn::kStageTransform | gdn::kStageScan, "prefill launch", shape, num_seqs,
-                         total_tokens, cu_seqlens, q, k, v, g, beta, o, state_pool, num_slots, init_slot,
-                         final_slot, start_pos, export_grid, export_states, export_offsets, num_export_states,
-                         workspace, workspace_bytes, stream);
-}
-
-gdn_status gdn_chunk_prefill_transform(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
-                                       const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
-                                       const float* g, const float* beta, void* o, float* state_pool,
-                                       int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
-                                       const int32_t* start_pos, int32_t export_grid, float* export_states,
-                                       const int32_t* export_offsets, int64_t num_export_states,
-                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return prefill_entry(gdn::kStageTransform, "prefill transform launch", shape, num_seqs, total_tokens,
-                         cu_seqlens, q, k, v, g, beta, o, state_pool, num_slots, init_slot, final_slot,
-                         start_pos, export_grid, export_states, export_offsets, num_export_states, workspace,
-                         workspace_bytes, stream);
-}
-
-gdn_status gdn_chunk_prefill_scan(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
-                                  const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
-                                  const float* g, const float* beta, void* o, float* state_pool,
-                                  int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
-                                  const int32_t* start_pos, int32_t export_grid, float* export_states,
-                                  const int32_t* export_offsets, int64_t num_export_states, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
-    return prefill_entry(gdn::kStageScan, "prefill scan launch", shape, num_seqs, total_tokens, cu_seqlens, q,
-                         k, v, g, beta, o, state_pool, num_slots, init_slot, final_slot, start_pos, export_grid,
-                         export_states, export_offsets, num_export_states, workspace, workspace_bytes, stream);
+                                          stream),
+                      "prefill launch");
 }
 
 gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const int32_t* slot_in,
@@ -328,7 +289,7 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const
                                                        num_slots, init_slot, final_slot, start_pos,
                                                        export_grid, export_states, export_offsets,
                                                        num_export_states, workspace),
-                                          gdn::kStageTransform | gdn::kStageScan, stream),
+                                          stream),
                       "mixed-step prefill launch");
 }
 

@@ -64,6 +64,18 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float4 v) {
 
 constexpr int kThreads = 256;
 
+// State traffic is touched once per call: stream it with non-temporal loads and
+// stores so it neither evicts nor waits on cache lines other work could reuse.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_state(const float* p) {
+    const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_state(float* p, float4 v) {
+    const f32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(p));
+}
+
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int TPR = DV / 4;          // threads per state row
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     float4 s[R];
 #pragma unroll
     for (int m = 0; m < R; ++m)
-        s[m] = *reinterpret_cast<const float4*>(src + (size_t)(rg + RG * m) * DV + 4 * c4);
+        s[m] = load_state(src + (size_t)(rg + RG * m) * DV + 4 * c4);
 
     __shared__ float kq[2][DK];
     __shared__ float4 red[2][RG][TPR];
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         float* dst = a.pool + ((size_t)sout * a.H_v + h) * (size_t)(DK * DV);
 #pragma unroll
         for (int m = 0; m < R; ++m)
-            *reinterpret_cast<float4*>(dst + (size_t)(rg + RG * m) * DV + 4 * c4) = s[m];
+            store_state(dst + (size_t)(rg + RG * m) * DV + 4 * c4, s[m]);
     }
     red[1][rg][c4] = po;
     __syncthreads();

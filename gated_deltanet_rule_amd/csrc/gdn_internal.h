@@ -52,14 +52,11 @@ struct PrefillArgs {
     void* workspace;
 };
 
-// Upper bound on the number of 64-token chunks for num_seqs sequences holding
-// total_tokens tokens, whatever the split and start offsets.
-int64_t max_chunks(int num_seqs, int64_t total_tokens);
+// Device scratch the prefill needs (none: every chunk's intermediates stay in LDS
+// and registers).
 size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_tokens);
-// stages: 1 = the UT transform (chunk table + T per chunk into the workspace),
-// 2 = the chunk scan (reads the workspace), 3 = both.
-constexpr int kStageTransform = 1;
-constexpr int kStageScan = 2;
-hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
+// Value heads that share one workgroup (and its staged Q and K).
+int prefill_heads_per_group(int dtype, int H_k, int H_v);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -12,30 +12,38 @@
 //     G   = inclusive cumsum of g inside the chunk,  gamma = e^G
 //     A   = strictly lower part of diag(beta) (K K^T) o D,   D[r][s] = e^(G_r - G_s)
 //     T   = (I + A)^-1
-//     U~  = (T diag(beta)) V,   W = (T diag(beta gamma)) K,   U = U~ - W S0
+//     T1  = T diag(beta),   T2 = T diag(beta gamma)
+//     U   = T1 V - T2 (K S0)                       (= U~ - W S0 with W = T2 K)
 //     O   = scale (diag(gamma) Q S0 + (Q K^T o D o lower-incl-diagonal) U)
 //     S1  = gamma_last S0 + K^T (diag(e^(G_last - G)) U)
-// Three kernels:
-//   prep_kernel   one workgroup: per-sequence chunk counts on the absolute 64-token
-//                 grid, their prefix sum, and the chunk table (sequence, first token,
-//                 length).
-//   tsolve_kernel one wave per (chunk, value head), all chunks at once: K K^T on
-//                 MFMA, the decay mask, and T by forward substitution in fp32 (lane j
-//                 owns column j).  T goes to the workspace in fp32.
-//   chain_kernel  one workgroup per (sequence, value head): the chunks of a sequence
-//                 in order.  Each wave owns a 32-column strip of d_v and keeps its
-//                 part of S in MFMA accumulator registers (fp32) for the whole
-//                 sequence; every product is an MFMA with fp32 accumulation.  The
-//                 d_v columns of S, U and O are independent, so the strips never
-//                 exchange data; shared operands (W, P, K, Q, T) go through LDS.
+//
+// One kernel.  A workgroup owns one sequence and HG value heads that share a key
+// head (HG = 2 for bf16 inputs when the GQA group size is even, else 1) and walks
+// the sequence's chunks in order.  Per value head, d_v is split into 32-column
+// strips, one wave each; a wave keeps its strip of S (d_k x 32, fp32) in MFMA
+// accumulator registers for the whole sequence.  The d_v columns of S, U and O are
+// independent, so strips never exchange data.  Per chunk:
+//   load     Q and K rows (shared by the HG heads) from the registers they were
+//            prefetched into during the previous chunk; V fragments likewise
+//   phase 1  gates by a wave scan; K K^T and Q K^T (lower tiles, shared by the HG
+//            heads) and Z = K S for each strip, on MFMA
+//   phase 2  A for each head into LDS (fp32)
+//   phase 3  T = (I + A)^-1 in place, one wave per head: the 16x16 diagonal blocks by
+//            forward substitution (lane 16b + j owns column j of block b), then
+//            T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj column block by column block on
+//            fp32 MFMA, each T_ij overwriting A_ij (its last use)
+//   phase 4  T1 and -T2, split once per chunk into LDS (all threads)
+//   phase 5  P into LDS; U = T1 V + (-T2) Z; O = gamma o (Q S) + P U; the state
+//            update; the grid export
 // Precision.  For bf16 inputs the MFMAs are 16x16x32 bf16.  q, k and v are exact in
-// bf16; the derived operands that carry most of the rounding error -- T (folded with
-// beta or beta gamma) and U (folded with the decay) -- enter as a hi + lo pair of
-// bf16 values (x = hi + lo to about 2^-17), i.e. two MFMAs against the exact
-// operand.  W, P and S enter as single bf16 values.  For fp32 inputs the MFMAs are
-// 16x16x4 fp32 and nothing is split.  States, accumulators, gates and T's solve
-// are fp32.  A sequence's work never depends on the other sequences of the call, so
-// its results are bitwise independent of its batch-mates.
+// bf16; the derived operands that carry most of the rounding error -- T1, T2 and
+// the decayed U -- enter as a hi + lo pair of bf16 values (x = hi + lo to about
+// 2^-17), two MFMAs against the other operand.  Z, P and S enter as single bf16
+// values.  For fp32 inputs the MFMAs are 16x16x4 fp32 and nothing is split.
+// States, accumulators, gates and T's solve are fp32.  A sequence's work never
+// depends on the other sequences of the call, so its results are bitwise
+// independent of its batch-mates; the chunks lie on the absolute 64-token grid, so
+// a resume from an exported grid state continues with the same arithmetic.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -218,9 +226,10 @@ __device__ __forceinline__ void zero16(void* dst) {
     *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// ---------------------------------------------------------------- prep kernel
 
-// Chunks of sequence i lie on the absolute 64-token grid: with a = start_pos % 64,
+// ---------------------------------------------------------------- chunk geometry
+
+// Chunks of a sequence lie on the absolute 64-token grid: with a = start_pos % 64,
 // chunk c covers local tokens [max(0, 64c - a), min(L, 64(c+1) - a)).
 __device__ __forceinline__ int seq_chunks(int L, int a) { return L > 0 ? (a + L + kC - 1) / kC : 0; }
 
@@ -234,54 +243,6 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int i, int64_t T, i
     len = (int)(e - b);
 }
 
-__global__ __launch_bounds__(256) void prep_kernel(const int32_t* cu, const int32_t* start_pos, int N,
-                                                   int64_t T, int nc_max, int4* table,
-                                                   int32_t* seq_off) {
-    __shared__ int scan[256];
-    __shared__ int carry;
-    const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < N; base += 256) {
-        const int i = base + tid;
-        int n = 0, lo = 0, len = 0, a = 0;
-        if (i < N) {
-            seq_range(cu, i, T, lo, len);
-            a = start_pos ? (start_pos[i] & (kC - 1)) : 0;
-            n = seq_chunks(len, a);
-        }
-        scan[tid] = n;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {   // inclusive Hillis-Steele scan
-            const int t = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += t;
-            __syncthreads();
-        }
-        const int first = carry + scan[tid] - n;
-        if (i < N) {
-            seq_off[i] = first;
-            for (int c = 0; c < n; ++c) {
-                const int idx = first + c;
-                if (idx >= nc_max) break;
-                const int b0 = c * kC - a < 0 ? 0 : c * kC - a;
-                const int e0 = (c + 1) * kC - a > len ? len : (c + 1) * kC - a;
-                table[idx] = make_int4(i, lo + b0, e0 - b0, c);
-            }
-        }
-        __syncthreads();
-        if (tid == 255) carry += scan[255];
-        __syncthreads();
-    }
-    if (tid == 0) seq_off[N] = carry;
-}
-
-// ---------------------------------------------------------------- gates and T = (I + A)^-1
-
-// Per (chunk, value head) gate vectors written by the transform and read by the scan.
-constexpr int kGates = 5;
-enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_BG = 3, GATE_KDEC = 4 };
-
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele, fixed order).
 __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 #pragma unroll
@@ -292,167 +253,64 @@ __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
     return x;
 }
 
-// One wave per (chunk, value head).  Writes the chunk's gate vectors (G, e^G, beta,
-// beta e^G, e^(G_last - G)) and T = (I + A)^-1 in fp32.  T is formed blockwise: the
-// four 16x16 diagonal blocks by forward substitution (lane 16b + j owns column j of
-// block b), then the off-diagonal blocks column block by column block,
-//     T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj,
-// on fp32 MFMA, each T_ij overwriting A_ij (whose last use it is).
-template <typename E, int DK>
-__global__ __launch_bounds__(64) void tsolve_kernel(PrefillArgs a, const int4* table,
-                                                     const int32_t* seq_off, int nc_max, float* tws,
-                                                     float* gws) {
-    using M = Mma<E>;
-    constexpr int KLD = DK + Pad<E>::value;
-    constexpr int ALD = kC + 4;
-    constexpr int KBYTES = kC * KLD * (int)sizeof(E);
-    constexpr int ABYTES = kC * ALD * (int)sizeof(float);
-    // one buffer holds K while K K^T is formed, then A, then T (in place)
-    __shared__ __attribute__((aligned(16))) char buf[KBYTES > ABYTES ? KBYTES : ABYTES];
-    __shared__ float Gs[kC], bl[kC];
-    E* ks = reinterpret_cast<E*>(buf);
-    float* as = reinterpret_cast<float*>(buf);
+constexpr int kGates = 5;
+enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_BG = 3, GATE_KDEC = 4 };
 
-    const int c = blockIdx.x;
-    const int h = blockIdx.y;
-    const int total = min(seq_off[a.num_seqs], nc_max);
-    if (c >= total) return;
-    const int4 ent = table[c];
-    const int tok = ent.y, L = ent.z;
-    const int kh = h / (a.H_v / a.H_k);
-    const int lane = threadIdx.x;
-    const int li = lane & 15, g4 = lane >> 4;
+template <typename E>
+struct NSplit { static constexpr int value = 2; };   // bf16: hi + lo
+template <>
+struct NSplit<float> { static constexpr int value = 1; };
 
-    // K rows of the chunk -> LDS (zero past L)
-    constexpr int VPR = DK / Vec<E>::N;
-    const E* kg = static_cast<const E*>(a.k);
-    for (int idx = lane; idx < kC * VPR; idx += 64) {
-        const int r = idx / VPR, vi = idx - r * VPR;
-        E* dst = ks + r * KLD + vi * Vec<E>::N;
-        if (r < L) copy16(dst, kg + ((size_t)(tok + r) * a.H_k + kh) * DK + vi * Vec<E>::N);
-        else zero16(dst);
-    }
-    // gates: lane s holds token s (g = beta = 0 past L, so G is flat there)
-    const float gs = lane < L ? a.g[(size_t)(tok + lane) * a.H_v + h] : 0.f;
-    const float bs = lane < L ? a.beta[(size_t)(tok + lane) * a.H_v + h] : 0.f;
-    const float G = wave_inclusive_sum(gs, lane);
-    const float G_last = __shfl(G, kC - 1, 64);
-    const float gam = expf(G);
-    float* gout = gws + ((size_t)c * a.H_v + h) * (kGates * kC);
-    gout[GATE_G * kC + lane] = G;
-    gout[GATE_GAM * kC + lane] = gam;
-    gout[GATE_BET * kC + lane] = bs;
-    gout[GATE_BG * kC + lane] = bs * gam;
-    gout[GATE_KDEC * kC + lane] = expf(G_last - G);
-    Gs[lane] = G;
-    bl[lane] = bs;
-    __syncthreads();
+template <typename E, int DK, int HG>
+struct ScanSmem {
+    static constexpr int QLD = DK + Pad<E>::value;      // Q and K rows
+    static constexpr int ALD = kC + 4;                  // fp32 A / T rows
+    static constexpr int TLD = kC + Pad<E>::value;      // T1, T2 rows (operand type)
+    static constexpr int PLD = kC + Pad<E>::value;      // P rows
+    static constexpr int NS = NSplit<E>::value;
+    E q[kC * QLD];
+    E k[kC * QLD];
+    struct Head {
+        union {
+            float a[kC * ALD];    // A, then T in place (phases 2-4)
+            E p[kC * PLD];        // then P (phase 5)
+        };
+        E t1[NS][kC * TLD];       // T diag(beta), hi [+ lo]
+        E t2[NS][kC * TLD];       // -T diag(beta gamma), hi [+ lo]
+        float gate[kGates * kC];
+        float graw[kC];
+        float braw[kC];
+    } hd[HG];
+};
 
-    // K K^T for the 10 lower 16x16 tiles, kept in registers (products of exact inputs)
-    f32x4 kk_t[10];
-    {
-        int t = 0;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt <= mt; ++nt, ++t) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-                for (int kk = 0; kk < DK / M::KSTEP; ++kk)
-                    acc = M::mma(M::row_nat(ks + (16 * mt + li) * KLD, kk, g4),
-                                 M::row_nat(ks + (16 * nt + li) * KLD, kk, g4), acc);
-                kk_t[t] = acc;
-            }
-    }
-    __syncthreads();   // K no longer needed: the buffer becomes A
-    for (int idx = lane; idx < kC * ALD; idx += 64) as[idx] = 0.f;
-    __syncthreads();
-    {
-        int t = 0;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt <= mt; ++nt, ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                    if (s < r) as[r * ALD + s] = bl[r] * kk_t[t][i] * expf(Gs[r] - Gs[s]);
-                }
-    }
-    __syncthreads();
-
-    // diagonal blocks: lane (b, j) forms column j of (I + A_bb)^-1
-    {
-        const int b = g4, j = li;
-        const float* Ab = as + (16 * b) * ALD + 16 * b;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc = fmaf(-Ab[r * ALD + s], t[s], acc);
-            t[r] = r < j ? 0.f : (r == j ? 1.f : acc);
-        }
-        __syncthreads();
-        float* Tb = as + (16 * b) * ALD + 16 * b;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tb[r * ALD + j] = t[r];
-    }
-    __syncthreads();
-
-    // off-diagonal blocks on fp32 MFMA (16x16x4): X = sum_k A_ik T_kj, then T_ij = -T_ii X
-#pragma unroll
-    for (int jb = 0; jb < 3; ++jb) {
-#pragma unroll
-        for (int ib = jb + 1; ib < 4; ++ib) {
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = jb; kb < ib; ++kb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    X = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        as[(16 * ib + li) * ALD + 16 * kb + 4 * q + g4],     // A_ik[m][4q + g]
-                        as[(16 * kb + 4 * q + g4) * ALD + 16 * jb + li],     // T_kj[4q + g][n]
-                        X, 0, 0, 0);
-            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)   // B from X's registers: element q is row 4g + q
-                Y = __builtin_amdgcn_mfma_f32_16x16x4f32(as[(16 * ib + li) * ALD + 16 * ib + 4 * g4 + q], X[q],
-                                                         Y, 0, 0, 0);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) as[(16 * ib + 4 * g4 + i) * ALD + 16 * jb + li] = -Y[i];
-            __syncthreads();
-        }
-    }
-
-    float* out = tws + ((size_t)c * a.H_v + h) * (kC * kC);
-    for (int idx = lane; idx < kC * kC / 4; idx += 64) {
-        const int r = idx >> 4, s4 = (idx & 15) * 4;
-        *reinterpret_cast<float4*>(out + r * kC + s4) = *reinterpret_cast<const float4*>(as + r * ALD + s4);
-    }
+// split an fp32 value into the operand type: hi (+ lo for bf16)
+template <typename E>
+__device__ __forceinline__ void split_store(E* hi, E* lo, int idx, float x);
+template <>
+__device__ __forceinline__ void split_store<__bf16>(__bf16* hi, __bf16* lo, int idx, float x) {
+    const __bf16 h = (__bf16)x;
+    hi[idx] = h;
+    lo[idx] = (__bf16)(x - (float)h);
+}
+template <>
+__device__ __forceinline__ void split_store<float>(float* hi, float*, int idx, float x) {
+    hi[idx] = x;
 }
 
-// ---------------------------------------------------------------- the chunk chain
-
-template <typename E, int DK, int DV>
-struct ChainSmem {
-    static constexpr int QLD = DK + Pad<E>::value;      // Q rows
-    static constexpr int TTLD = kC + Pad<E>::value;     // K^T rows (one per d_k index, tokens along)
-    static constexpr int VLD = DV + Pad<E>::value;      // V rows
-    static constexpr int WLD = DK + Pad<E>::value;      // -W rows
-    static constexpr int TLD = kC + 4;                  // fp32 T rows
-    static constexpr int PLD = kC + Pad<E>::value;      // P rows
-    E q[kC * QLD];
-    E kt[DK * TTLD];
-    union {
-        E v[kC * VLD];    // V (until U~ is formed)
-        E w[kC * WLD];    // then -W
-    };
-    float t[kC * TLD];
-    E p[kC * PLD];
-    float gate[kGates * kC];
-};
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::pair row_pair_nat(const E* hi, const E* lo, int ks, int g) {
+    typename Mma<E>::pair p;
+    p.hi = Mma<E>::row_nat(hi, ks, g);
+    if constexpr (NSplit<E>::value == 2) p.lo = Mma<E>::row_nat(lo, ks, g);
+    return p;
+}
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::pair row_pair_fromc(const E* hi, const E* lo, int ks, int g) {
+    typename Mma<E>::pair p;
+    p.hi = Mma<E>::row_fromc(hi, ks, g);
+    if constexpr (NSplit<E>::value == 2) p.lo = Mma<E>::row_fromc(lo, ks, g);
+    return p;
+}
 
 // smallest k index that step ks of each order covers
 template <typename M>
@@ -460,39 +318,46 @@ __device__ __forceinline__ int kmin_nat(int ks) { return ks * M::KSTEP; }
 template <typename M>
 __device__ __forceinline__ int kmin_fromc(int ks) { return M::KSTEP == 32 ? 32 * ks : 16 * (ks >> 2); }
 
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int nc_max, const float* tws,
-                  const float* gws) {
-    using M = Mma<E>;
-    using S = ChainSmem<E, DK, DV>;
-    constexpr int NW = DV / 32;            // waves; wave w owns columns [32w, 32w + 32)
-    constexpr int NT = NW * 64;            // threads
-    constexpr int MT_S = DK / 16;          // 16-row tiles of the state
-    constexpr int KS_DK = DK / M::KSTEP;   // k steps over d_k
-    constexpr int KS_C = kC / M::KSTEP;    // k steps over the chunk
-    constexpr int VN = Vec<E>::N;
-    __shared__ __attribute__((aligned(16))) S sm;
+// ---------------------------------------------------------------- the scan kernel
 
-    const int seq = blockIdx.x / a.H_v;
-    const int h = blockIdx.x - seq * a.H_v;
-    const int kh = h / (a.H_v / a.H_k);
+template <typename E, int DK, int DV, int HG>
+__global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
+    using M = Mma<E>;
+    using SM = ScanSmem<E, DK, HG>;
+    constexpr int NWH = DV / 32;             // waves per value head
+    constexpr int NW = HG * NWH;             // waves
+    constexpr int NT = NW * 64;              // threads
+    constexpr int MT_S = DK / 16;            // 16-row tiles of the state
+    constexpr int KS_DK = DK / M::KSTEP;     // k steps over d_k
+    constexpr int KS_C = kC / M::KSTEP;      // k steps over the chunk
+    constexpr int VN = Vec<E>::N;            // elements per 16-byte vector
+    constexpr int VPR = DK / VN;             // 16-byte vectors per Q/K row
+    constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
+    constexpr int TPW = (16 + NW - 1) / NW;  // 16x16 tiles of a 64x64 matrix per wave
+    constexpr int NVF = KS_C * 2;            // V fragments per wave
+    static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
+    __shared__ __attribute__((aligned(16))) SM sm;
+
+    const int G = a.H_v / a.H_k;
+    const int GG = G / HG;
+    const int seq = blockIdx.x / (a.H_k * GG);
+    const int rem = blockIdx.x - seq * (a.H_k * GG);
+    const int kh = rem / GG;
+    const int h0 = kh * G + (rem - kh * GG) * HG;
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
-    const int lane = tid & 63;
-    const int li = lane & 15, g4 = lane >> 4;
-    const int col0 = 32 * wv;
-    const float* bet = sm.gate + GATE_BET * kC;
-    const float* bg = sm.gate + GATE_BG * kC;
-    const float* gam = sm.gate + GATE_GAM * kC;
-    const float* Gv = sm.gate + GATE_G * kC;
-    const float* kdec = sm.gate + GATE_KDEC * kC;
+    int lane = tid & 63;
+    const int hh = wv / NWH;                 // this wave's head within the group
+    const int h = h0 + hh;
+    const int col0 = 32 * (wv - hh * NWH);
+    typename SM::Head& hd = sm.hd[hh];
 
     const size_t SE = (size_t)DK * DV;
     // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
     f32x4 Sacc[MT_S][2];
     const int isl = a.init_slot ? a.init_slot[seq] : -1;
     if (isl >= 0 && isl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
         const float* src = a.pool + ((size_t)isl * a.H_v + h) * SE;
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
@@ -508,127 +373,279 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
             for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int total = min(seq_off[a.num_seqs], nc_max);
-    const int c_begin = min(seq_off[seq], total);
-    const int c_end = min(seq_off[seq + 1], total);
+    int lo, len;
+    seq_range(a.cu_seqlens, seq, a.total_tokens, lo, len);
     const int64_t pos0 = a.start_pos ? a.start_pos[seq] : 0;
-    int seq_tok0 = 0;
-    if (c_begin < c_end) seq_tok0 = table[c_begin].y;
+    const int off64 = (int)(pos0 & (kC - 1));
+    const int nchunks = seq_chunks(len, off64);
 
     const E* qg = static_cast<const E*>(a.q);
     const E* kg = static_cast<const E*>(a.k);
     const E* vg = static_cast<const E*>(a.v);
     E* og = static_cast<E*>(a.o);
 
-    for (int c = c_begin; c < c_end; ++c) {
-        const int4 ent = table[c];
-        const int tok = ent.y, L = ent.z;
+    // ---- prefetch registers: Q/K row vectors, this wave's V fragments, g/beta
+    uint4 pf[NPF];
+    typename M::frag vpf[NVF];
+    float gbpf = 0.f;
+    auto chunk_bounds = [&](int c, int& tok, int& L, int& e0) {
+        const int b0 = c * kC - off64 < 0 ? 0 : c * kC - off64;
+        e0 = (c + 1) * kC - off64 > len ? len : (c + 1) * kC - off64;
+        tok = lo + b0;
+        L = e0 - b0;
+    };
+    auto prefetch = [&](int c, int li, int g4) {
+        int tok, L, e0;
+        chunk_bounds(c, tok, L, e0);
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int i = tid + NT * j;
+            const int which = i / (kC * VPR);            // 0: Q, 1: K
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            const E* src = which == 0 ? qg : kg;
+            pf[j] = r < L ? *reinterpret_cast<const uint4*>(src + ((size_t)(tok + r) * a.H_k + kh) * DK + vi * VN)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KS_C; ++kk)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                typename M::frag f;
+                if constexpr (M::KSTEP == 32) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = M::nat(kk, g4, e);
+                        f[e] = s < L ? vg[((size_t)(tok + s) * a.H_v + h) * DV + col0 + 16 * nt + li] : (E)0.f;
+                    }
+                } else {
+                    const int s = M::nat(kk, g4, 0);
+                    f = s < L ? vg[((size_t)(tok + s) * a.H_v + h) * DV + col0 + 16 * nt + li] : (E)0.f;
+                }
+                vpf[kk * 2 + nt] = f;
+            }
+        if (tid < 2 * kC * HG) {                          // g then beta for each head
+            const int hx = tid / (2 * kC), which = (tid / kC) & 1, s = tid % kC;
+            const float* src = which == 0 ? a.g : a.beta;
+            gbpf = s < L ? src[(size_t)(tok + s) * a.H_v + h0 + hx] : 0.f;
+        }
+    };
+    if (nchunks > 0) prefetch(0, lane & 15, lane >> 4);
+
+    for (int c = 0; c < nchunks; ++c) {
+        int tok, L, e0;
+        chunk_bounds(c, tok, L, e0);
+        // Keep lane-derived addresses inside the loop: without this the compiler hoists
+        // every unrolled access's address out of the chunk loop and runs out of registers.
+        asm volatile("" : "+v"(lane));
+        const int li = lane & 15, g4 = lane >> 4;
         __syncthreads();   // the previous chunk is done with LDS
 
-        // ---- loads: Q rows, K transposed, V rows, T, gates
-        for (int idx = tid; idx < kC * (DK / VN); idx += NT) {
-            const int r = idx / (DK / VN), d0 = (idx - r * (DK / VN)) * VN;
-            E* dq = sm.q + r * S::QLD + d0;
-            if (r < L) copy16(dq, qg + ((size_t)(tok + r) * a.H_k + kh) * DK + d0);
-            else zero16(dq);
-        }
-        // K: consecutive threads take consecutive tokens, so the transposed LDS writes
-        // of a wave fall in consecutive addresses
-        for (int idx = tid; idx < kC * (DK / VN); idx += NT) {
-            const int r = idx & (kC - 1), d0 = (idx >> 6) * VN;
-            E kv[VN];
-            if (r < L) {
-                *reinterpret_cast<uint4*>(kv) =
-                    *reinterpret_cast<const uint4*>(kg + ((size_t)(tok + r) * a.H_k + kh) * DK + d0);
-            } else {
-                *reinterpret_cast<uint4*>(kv) = make_uint4(0u, 0u, 0u, 0u);
-            }
+        // ---- stage this chunk's inputs; prefetch the next chunk
 #pragma unroll
-            for (int e = 0; e < VN; ++e) sm.kt[(d0 + e) * S::TTLD + r] = kv[e];
+        for (int j = 0; j < NPF; ++j) {
+            const int i = tid + NT * j;
+            const int which = i / (kC * VPR);
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            E* dst = (which == 0 ? sm.q : sm.k) + r * SM::QLD + vi * VN;
+            *reinterpret_cast<uint4*>(dst) = pf[j];
         }
-        for (int idx = tid; idx < kC * (DV / VN); idx += NT) {
-            const int r = idx / (DV / VN), vi = idx - r * (DV / VN);
-            E* dv = sm.v + r * S::VLD + vi * VN;
-            if (r < L) copy16(dv, vg + ((size_t)(tok + r) * a.H_v + h) * DV + vi * VN);
-            else zero16(dv);
-        }
-        {
-            const float* tsrc = tws + ((size_t)c * a.H_v + h) * (kC * kC);
-            for (int idx = tid; idx < kC * kC / 4; idx += NT) {
-                const int r = idx >> 4, s4 = (idx & 15) * 4;
-                copy16(sm.t + r * S::TLD + s4, tsrc + r * kC + s4);
-            }
-            const float* gsrc = gws + ((size_t)c * a.H_v + h) * (kGates * kC);
-            for (int idx = tid; idx < kGates * kC / 4; idx += NT) copy16(sm.gate + 4 * idx, gsrc + 4 * idx);
+        typename M::frag vcur[NVF];
+#pragma unroll
+        for (int j = 0; j < NVF; ++j) vcur[j] = vpf[j];
+        if (tid < 2 * kC * HG) {
+            const int hx = tid / (2 * kC), which = (tid / kC) & 1, s = tid % kC;
+            (which == 0 ? sm.hd[hx].graw : sm.hd[hx].braw)[s] = gbpf;
         }
         __syncthreads();
 
-        // ---- phase A1: U~ = (T diag(beta)) V for this wave's strip (T is lower triangular:
-        //      steps wholly above the diagonal are skipped)
+        // ---- phase 1: gates; K K^T lower tiles
+        if (wv - hh * NWH == 0) {                          // first wave of each head
+            const float gs = hd.graw[lane];
+            const float bs = hd.braw[lane];
+            const float Gc = wave_inclusive_sum(gs, lane);
+            const float G_last = __shfl(Gc, kC - 1, 64);
+            const float gam = expf(Gc);
+            hd.gate[GATE_G * kC + lane] = Gc;
+            hd.gate[GATE_GAM * kC + lane] = gam;
+            hd.gate[GATE_BET * kC + lane] = bs;
+            hd.gate[GATE_BG * kC + lane] = bs * gam;
+            hd.gate[GATE_KDEC * kC + lane] = expf(G_last - Gc);
+        }
+        f32x4 kkt[TPW];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wv + NW * j;
+            const int mt = t >> 2, nt = t & 3;
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f};
+            if (t < 16 && nt <= mt) {
+#pragma unroll 2
+                for (int kk = 0; kk < KS_DK; ++kk)
+                    ak = M::mma(M::row_nat(sm.k + (16 * mt + li) * SM::QLD, kk, g4),
+                                M::row_nat(sm.k + (16 * nt + li) * SM::QLD, kk, g4), ak);
+            }
+            kkt[j] = ak;
+        }
+        __syncthreads();
+
+        // ---- phase 2: A for every head (zeros on and above the diagonal)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wv + NW * j;
+            if (t >= 16) continue;
+            const int mt = t >> 2, nt = t & 3;
+#pragma unroll
+            for (int x = 0; x < HG; ++x) {
+                const float* gt = sm.hd[x].gate;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
+                    const float val = s < r ? gt[GATE_BET * kC + r] * kkt[j][i] *
+                                                  expf(gt[GATE_G * kC + r] - gt[GATE_G * kC + s])
+                                            : 0.f;
+                    sm.hd[x].a[r * SM::ALD + s] = val;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 3: T = (I + A)^-1 in place, one wave per head
+        if (wv - hh * NWH == 0) {
+            float* as = hd.a;
+            constexpr int ALD = SM::ALD;
+            {
+                const int b = g4, j = li;
+                const float* Ab = as + (16 * b) * ALD + 16 * b;
+                float t[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int s = 0; s < r; ++s) acc = fmaf(-Ab[r * ALD + s], t[s], acc);
+                    t[r] = r < j ? 0.f : (r == j ? 1.f : acc);
+                }
+                __builtin_amdgcn_wave_barrier();
+                float* Tb = as + (16 * b) * ALD + 16 * b;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Tb[r * ALD + j] = t[r];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int jb = 0; jb < 3; ++jb) {
+#pragma unroll
+                for (int ib = jb + 1; ib < 4; ++ib) {
+                    f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = jb; kb < ib; ++kb)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            X = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                as[(16 * ib + li) * ALD + 16 * kb + 4 * q + g4],    // A_ik[m][4q + g]
+                                as[(16 * kb + 4 * q + g4) * ALD + 16 * jb + li],    // T_kj[4q + g][n]
+                                X, 0, 0, 0);
+                    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)   // B from X's registers: element q is row 4g + q
+                        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(as[(16 * ib + li) * ALD + 16 * ib + 4 * g4 + q],
+                                                                 X[q], Y, 0, 0, 0);
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) as[(16 * ib + 4 * g4 + i) * ALD + 16 * jb + li] = -Y[i];
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 4: T1 = T diag(beta) and -T2 = -T diag(beta gamma), split, all threads
+#pragma unroll
+        for (int x = 0; x < HG; ++x) {
+            typename SM::Head& hx = sm.hd[x];
+            for (int idx = tid; idx < kC * kC / 4; idx += NT) {
+                const int r = idx >> 4, s4 = (idx & 15) * 4;
+                const float4 tv = *reinterpret_cast<const float4*>(hx.a + r * SM::ALD + s4);
+                const float tr[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s4 + e;
+                    split_store<E>(hx.t1[0], hx.t1[SM::NS - 1], r * SM::TLD + s, tr[e] * hx.gate[GATE_BET * kC + s]);
+                    split_store<E>(hx.t2[0], hx.t2[SM::NS - 1], r * SM::TLD + s, -tr[e] * hx.gate[GATE_BG * kC + s]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 5a: P for every head (into the dead A/T space); Z = K S; U = T1 V + (-T2) Z
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wv + NW * j;
+            if (t >= 16) continue;
+            const int mt = t >> 2, nt = t & 3;
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f};
+            if (nt <= mt) {
+#pragma unroll 2
+                for (int kk = 0; kk < KS_DK; ++kk)
+                    aq = M::mma(M::row_nat(sm.q + (16 * mt + li) * SM::QLD, kk, g4),
+                                M::row_nat(sm.k + (16 * nt + li) * SM::QLD, kk, g4), aq);
+            }
+#pragma unroll
+            for (int x = 0; x < HG; ++x) {
+                const float* gt = sm.hd[x].gate;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
+                    const float val = s <= r ? aq[i] * expf(gt[GATE_G * kC + r] - gt[GATE_G * kC + s]) : 0.f;
+                    sm.hd[x].p[r * SM::PLD + s] = (E)val;
+                }
+            }
+        }
         f32x4 Uacc[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            Uacc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Uacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Uacc[mt][0] = Uacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
                 if (kmin_nat<M>(kk) > 16 * mt + 15) continue;
-                const typename M::pair ta = M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, bet);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    Uacc[mt][nt] = M::mma_sa(ta, M::col_nat(sm.v, S::VLD, col0 + 16 * nt + li, kk, g4),
-                                             Uacc[mt][nt]);
+                const typename M::pair ta = row_pair_nat<E>(hd.t1[0] + (16 * mt + li) * SM::TLD,
+                                                            hd.t1[SM::NS - 1] + (16 * mt + li) * SM::TLD, kk, g4);
+                Uacc[mt][0] = M::mma_sa(ta, vcur[kk * 2 + 0], Uacc[mt][0]);
+                Uacc[mt][1] = M::mma_sa(ta, vcur[kk * 2 + 1], Uacc[mt][1]);
             }
         }
-        __syncthreads();   // V is dead: its space takes -W
-
-        // ---- phase A2 + B (shared, split over the waves):
-        //      -W = -(T diag(beta gamma)) K  and  P = (Q K^T) o D o lower-incl-diagonal
-        for (int t = wv; t < 4 * (DK / 16); t += NW) {
-            const int mt = t / (DK / 16), nt = t - mt * (DK / 16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        {
+            f32x4 Zacc[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Zacc[mt][0] = Zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS_DK; ++kk) {
+                const typename M::frag sb0 = M::acc_fromc(&Sacc[0][0], kk, 2);
+                const typename M::frag sb1 = M::acc_fromc(&Sacc[0][1], kk, 2);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const typename M::frag ka = M::row_fromc(sm.k + (16 * mt + li) * SM::QLD, kk, g4);
+                    Zacc[mt][0] = M::mma(ka, sb0, Zacc[mt][0]);
+                    Zacc[mt][1] = M::mma(ka, sb1, Zacc[mt][1]);
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
-                if (kmin_nat<M>(kk) > 16 * mt + 15) continue;
-                acc = M::mma_sa(M::row_nat_scaled_split(sm.t + (16 * mt + li) * S::TLD, kk, g4, bg),
-                                M::row_nat(sm.kt + (16 * nt + li) * S::TTLD, kk, g4), acc);
-            }
+                const typename M::frag zb0 = M::acc_fromc(&Zacc[0][0], kk, 2);
+                const typename M::frag zb1 = M::acc_fromc(&Zacc[0][1], kk, 2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sm.w[(16 * mt + 4 * g4 + i) * S::WLD + 16 * nt + li] = (E)(-acc[i]);
-        }
-        for (int t = wv; t < 16; t += NW) {
-            const int mt = t >> 2, nt = t & 3;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (nt <= mt) {
-#pragma unroll 4
-                for (int kk = 0; kk < KS_DK; ++kk)
-                    acc = M::mma(M::row_nat(sm.q + (16 * mt + li) * S::QLD, kk, g4),
-                                 M::col_nat(sm.kt, S::TTLD, 16 * nt + li, kk, g4), acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                const float val = s <= r ? acc[i] * expf(Gv[r] - Gv[s]) : 0.f;
-                sm.p[r * S::PLD + s] = (E)val;
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (kmin_fromc<M>(kk) > 16 * mt + 15) continue;
+                    const typename M::pair ta = row_pair_fromc<E>(hd.t2[0] + (16 * mt + li) * SM::TLD,
+                                                                  hd.t2[SM::NS - 1] + (16 * mt + li) * SM::TLD, kk, g4);
+                    Uacc[mt][0] = M::mma_sa(ta, zb0, Uacc[mt][0]);
+                    Uacc[mt][1] = M::mma_sa(ta, zb1, Uacc[mt][1]);
+                }
             }
         }
-        __syncthreads();
+        // this chunk's inputs are consumed: fetch the next chunk's while the rest runs
+        if (c + 1 < nchunks) prefetch(c + 1, li, g4);
+        __syncthreads();   // P is complete
 
-        // ---- phase C: U = U~ + (-W) S
-#pragma unroll
-        for (int kk = 0; kk < KS_DK; ++kk) {
-            const typename M::frag sb0 = M::acc_fromc(&Sacc[0][0], kk, 2);
-            const typename M::frag sb1 = M::acc_fromc(&Sacc[0][1], kk, 2);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const typename M::frag wa = M::row_fromc(sm.w + (16 * mt + li) * S::WLD, kk, g4);
-                Uacc[mt][0] = M::mma(wa, sb0, Uacc[mt][0]);
-                Uacc[mt][1] = M::mma(wa, sb1, Uacc[mt][1]);
-            }
-        }
-
-        // ---- phase D: O = gamma o (Q S) + P U, one 16-column tile at a time
+        // ---- phase 5b: O = gamma o (Q S) + P U, one 16-column tile at a time
+        const float* gam = hd.gate + GATE_GAM * kC;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 Oacc[4];
@@ -639,7 +656,7 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
                 const typename M::frag sb = M::acc_fromc(&Sacc[0][nt], kk, 2);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
-                    Oacc[mt] = M::mma(M::row_fromc(sm.q + (16 * mt + li) * S::QLD, kk, g4), sb, Oacc[mt]);
+                    Oacc[mt] = M::mma(M::row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4), sb, Oacc[mt]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -651,7 +668,7 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (kmin_fromc<M>(kk) > 16 * mt + 15) continue;
-                    Oacc[mt] = M::mma_sb(M::row_fromc(sm.p + (16 * mt + li) * S::PLD, kk, g4), ub, Oacc[mt]);
+                    Oacc[mt] = M::mma_sb(M::row_fromc(hd.p + (16 * mt + li) * SM::PLD, kk, g4), ub, Oacc[mt]);
                 }
             }
 #pragma unroll
@@ -664,8 +681,9 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
                 }
         }
 
-        // ---- phase E: S = gamma_last S + K^T (diag(e^(G_last - G)) U)
+        // ---- phase 5c: S = gamma_last S + K^T (diag(e^(G_last - G)) U)
         const float gl_last = gam[kC - 1];
+        const float* kdec = hd.gate + GATE_KDEC * kC;
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
@@ -679,7 +697,7 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
             const typename M::pair ub1 = M::acc_fromc_split(&Uacc[0][1], kk, 2, g4, kdec);
 #pragma unroll
             for (int mt = 0; mt < MT_S; ++mt) {
-                const typename M::frag ka = M::row_fromc(sm.kt + (16 * mt + li) * S::TTLD, kk, g4);
+                const typename M::frag ka = M::col_fromc(sm.k, SM::QLD, 16 * mt + li, kk, g4);
                 Sacc[mt][0] = M::mma_sb(ka, ub0, Sacc[mt][0]);
                 Sacc[mt][1] = M::mma_sb(ka, ub1, Sacc[mt][1]);
             }
@@ -687,7 +705,7 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
 
         // ---- export on the grid
         if (a.export_grid > 0) {
-            const int64_t p_end = pos0 + (tok + L - seq_tok0);
+            const int64_t p_end = pos0 + e0;
             if (p_end % a.export_grid == 0) {
                 const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
                 const int64_t idx = (int64_t)a.export_offsets[seq] + m;
@@ -707,6 +725,7 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
 
     const int fsl = a.final_slot ? a.final_slot[seq] : -1;
     if (fsl >= 0 && fsl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
         float* dst = a.pool + ((size_t)fsl * a.H_v + h) * SE;
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
@@ -718,78 +737,39 @@ void chain_kernel(PrefillArgs a, const int4* table, const int32_t* seq_off, int 
     }
 }
 
-// ---------------------------------------------------------------- workspace layout
-
-struct Layout {
-    size_t table, seq_off, tws, gws, total;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-Layout layout(int H_v, int num_seqs, int64_t total_tokens) {
-    const int64_t nc = max_chunks(num_seqs, total_tokens);
-    Layout l;
-    l.table = 0;
-    l.seq_off = align256(l.table + (size_t)nc * sizeof(int4));
-    l.tws = align256(l.seq_off + (size_t)(num_seqs + 1) * sizeof(int32_t));
-    l.gws = align256(l.tws + (size_t)nc * H_v * kC * kC * sizeof(float));
-    l.total = align256(l.gws + (size_t)nc * H_v * kGates * kC * sizeof(float));
-    return l;
+template <typename E, int DK, int DV, int HG>
+hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
+    const int G = a.H_v / a.H_k;
+    const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG);
+    hipLaunchKernelGGL((scan_kernel<E, DK, DV, HG>), dim3(blocks), dim3(HG * DV * 2), 0, stream, a);
+    return hipGetLastError();
 }
 
-// stage bit 1: prep + tsolve (fills the workspace); stage bit 2: the chunk chain
-template <typename E, int DK, int DV>
-hipError_t launch_typed(const PrefillArgs& a, int stages, hipStream_t stream) {
-    const Layout l = layout(a.H_v, a.num_seqs, a.total_tokens);
-    char* ws = static_cast<char*>(a.workspace);
-    int4* table = reinterpret_cast<int4*>(ws + l.table);
-    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + l.seq_off);
-    float* tws = reinterpret_cast<float*>(ws + l.tws);
-    float* gws = reinterpret_cast<float*>(ws + l.gws);
-    const int nc_max = (int)max_chunks(a.num_seqs, a.total_tokens);
-
-    if (stages & 1) {
-        hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.start_pos,
-                           a.num_seqs, a.total_tokens, nc_max, table, seq_off);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((tsolve_kernel<E, DK>), dim3(nc_max, a.H_v), dim3(64), 0, stream, a, table,
-                           seq_off, nc_max, tws, gws);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    if (stages & 2) {
-        hipLaunchKernelGGL((chain_kernel<E, DK, DV>), dim3(a.num_seqs * a.H_v), dim3(DV * 2), 0, stream,
-                           a, table, seq_off, nc_max, tws, gws);
-        return hipGetLastError();
-    }
-    return hipSuccess;
-}
-
-template <typename E>
-hipError_t launch_dims(const PrefillArgs& a, int stages, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_typed<E, 128, 128>(a, stages, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_typed<E, 128, 64>(a, stages, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_typed<E, 64, 128>(a, stages, stream);
-    return launch_typed<E, 64, 64>(a, stages, stream);
+template <typename E, int HG>
+hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_typed<E, 128, 128, HG>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_typed<E, 128, 64, HG>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_typed<E, 64, 128, HG>(a, stream);
+    return launch_typed<E, 64, 64, HG>(a, stream);
 }
 
 }  // namespace
 
-int64_t max_chunks(int num_seqs, int64_t total_tokens) {
-    // each sequence adds at most one partial chunk at each end
-    return (total_tokens + kC - 1) / kC + 2 * (int64_t)num_seqs;
+size_t prefill_workspace_bytes(int, int, int, int64_t) { return 0; }
+
+int prefill_heads_per_group(int dtype, int H_k, int H_v) {
+    // Two value heads that share a key head go to one workgroup (bf16 only: the fp32
+    // operand buffers of two heads do not fit in LDS).
+    return (dtype == 1 && (H_v / H_k) % 2 == 0) ? 2 : 1;
 }
 
-size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_tokens) {
-    (void)dtype;
-    return layout(H_v, num_seqs, total_tokens).total;
-}
-
-hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    if (a.dtype == 1) return launch_dims<__bf16>(a, stages, stream);
-    return launch_dims<float>(a, stages, stream);
+    if (a.dtype == 1) {
+        if (prefill_heads_per_group(a.dtype, a.H_k, a.H_v) == 2) return launch_dims<__bf16, 2>(a, stream);
+        return launch_dims<__bf16, 1>(a, stream);
+    }
+    return launch_dims<float, 1>(a, stream);
 }
 
 }  // namespace gdn

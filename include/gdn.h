@@ -89,8 +89,10 @@ typedef struct {
 } gdn_shape;
 
 /* Bytes of device workspace that gdn_chunk_prefill / gdn_mixed_step need for
- * num_seqs sequences holding total_tokens tokens (an upper bound that covers
- * any split of the tokens).  0 for an unsupported shape. */
+ * num_seqs sequences holding total_tokens tokens.  The current kernels keep every
+ * intermediate in LDS and registers, so this is 0 (the argument is kept so that a
+ * future kernel can take scratch without an ABI change); it is also 0 for an
+ * unsupported shape. */
 size_t gdn_chunk_prefill_workspace_size(const gdn_shape* shape, int32_t num_seqs,
                                         int64_t total_tokens);
 
@@ -150,7 +152,8 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows,
  *   num_export_states  how many states export_states holds; an export whose index
  *              would reach it is dropped (the kernels never write past the buffer).
  *   workspace  device scratch of at least gdn_chunk_prefill_workspace_size() bytes,
- *              256-byte aligned; its contents need no initialisation.
+ *              256-byte aligned, contents need no initialisation; may be NULL when
+ *              that size is 0.
  *   num_seqs == 0 or total_tokens == 0 is a no-op returning GDN_OK (a zero-length
  *   sequence inside a batch copies its initial state to its final slot).
  */
@@ -162,40 +165,6 @@ gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t t
                              int32_t export_grid, float* export_states,
                              const int32_t* export_offsets, int64_t num_export_states,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/*
- * The two stages of gdn_chunk_prefill, callable apart: gdn_chunk_prefill is exactly
- * gdn_chunk_prefill_transform followed by gdn_chunk_prefill_scan with the same
- * arguments and workspace, on one stream.
- *   gdn_chunk_prefill_transform  the state-independent part of every chunk (the chunk
- *       table on the absolute 64-token grid and the UT transform T = (I + A)^-1 of the
- *       WY form), written to the workspace; reads only cu_seqlens, start_pos, k, g and
- *       beta.  All chunks are processed in parallel.
- *   gdn_chunk_prefill_scan  the sequential chunk scan of each (sequence, value head):
- *       reads the workspace the transform filled, writes o, the final states and the
- *       exports.
- *   Defined by: "[V1][Hybrid] GatedDeltaNet Automatic Prefix Caching", section
- *   "Purpose" (the chunk kernel and its returned per-chunk states).  Arguments,
- *   validation and errors are those of gdn_chunk_prefill (both stages validate all of
- *   them).  Use: scheduling the transform apart from the scan (for example on work
- *   that does not depend on the previous state) and timing each stage.
- */
-gdn_status gdn_chunk_prefill_transform(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
-                                       const int32_t* cu_seqlens, const void* q, const void* k,
-                                       const void* v, const float* g, const float* beta, void* o,
-                                       float* state_pool, int32_t num_slots, const int32_t* init_slot,
-                                       const int32_t* final_slot, const int32_t* start_pos,
-                                       int32_t export_grid, float* export_states,
-                                       const int32_t* export_offsets, int64_t num_export_states,
-                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
-gdn_status gdn_chunk_prefill_scan(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
-                                  const int32_t* cu_seqlens, const void* q, const void* k,
-                                  const void* v, const float* g, const float* beta, void* o,
-                                  float* state_pool, int32_t num_slots, const int32_t* init_slot,
-                                  const int32_t* final_slot, const int32_t* start_pos,
-                                  int32_t export_grid, float* export_states,
-                                  const int32_t* export_offsets, int64_t num_export_states,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One mixed decode-plus-prefill step: tokens [0, num_decode_rows) are cached decode

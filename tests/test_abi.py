@@ -4,7 +4,7 @@ clear message before anything is enqueued.
 
 Every call here is built to fail host validation: besides the argument under test,
 each one carries a second invalid argument that validation checks later (a NULL
-slot_out for decode, a zero workspace size for prefill), so no call can ever reach a
+slot_out for decode, a NULL init_slot for prefill), so no call can ever reach a
 kernel launch, on a machine with or without a GPU."""
 import ctypes
 import os
@@ -29,8 +29,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"gdn_chunk_prefill_workspace_size", "gdn_recurrent_decode", "gdn_chunk_prefill",
-                          "gdn_chunk_prefill_transform", "gdn_chunk_prefill_scan", "gdn_mixed_step",
-                          "gdn_last_error"}
+                          "gdn_mixed_step", "gdn_last_error"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -38,17 +37,12 @@ def test_exports_every_declared_symbol():
 
 
 def test_workspace_size():
+    """The prefill keeps every intermediate in LDS and registers: no scratch needed."""
     lib = B.library()
     s = B.make_shape(16, 32, 128, 128, B.GDN_BF16, 0.1)
-    n16 = lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s), 16, 16 * 8192)
-    chunks = (16 * 8192 + 63) // 64 + 2 * 16
-    assert n16 >= chunks * 32 * 64 * 64 * 4            # one fp32 T matrix per (chunk, head)
-    assert n16 % 256 == 0
-    s32 = B.make_shape(16, 32, 128, 128, B.GDN_F32, 0.1)
-    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s32), 16, 16 * 8192) == n16
+    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s), 16, 16 * 8192) == 0
     bad = B.make_shape(3, 32, 128, 128, B.GDN_BF16, 0.1)
     assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(bad), 16, 1000) == 0
-    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(s), 0, 0) > 0
 
 
 FAKE = 0x100000           # a 16-byte aligned stand-in address that is never dereferenced
@@ -63,12 +57,14 @@ def _decode(shape=None, num_rows=4, q=FAKE, num_slots=8, slot_out=None):
 
 
 def _prefill(shape=None, num_seqs=2, total_tokens=100, export_grid=0, q=FAKE, cu=FAKE, ws_bytes=0,
-             num_export=0):
+             num_export=0, init_slot=None, export_offsets=FAKE):
+    # guard: init_slot is NULL unless a test passes one, and validation rejects that
+    # after every check the tests below exercise
     lib = B.library()
     shape = shape or B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
     st = lib.gdn_chunk_prefill(ctypes.byref(shape), num_seqs, total_tokens, cu, q, FAKE, FAKE, FAKE, FAKE,
-                               FAKE, FAKE, 8, FAKE, FAKE, None, export_grid, FAKE, FAKE, num_export, FAKE,
-                               ws_bytes, None)
+                               FAKE, FAKE, 8, init_slot, FAKE, None, export_grid, FAKE, export_offsets,
+                               num_export, FAKE, ws_bytes, None)
     return st, B.gdn_last_error()
 
 
@@ -112,28 +108,17 @@ def test_prefill_validation():
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "total_tokens -5" in msg
     st, msg = _prefill(cu=None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "cu_seqlens is NULL" in msg
-    st, msg = _prefill(q=FAKE + 8)
+    # q is checked after init_slot; the guard here is a NULL export_offsets, checked after q
+    st, msg = _prefill(q=FAKE + 8, init_slot=FAKE, export_grid=64, export_offsets=None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "q (" in msg and "aligned" in msg
+    st, msg = _prefill(init_slot=FAKE, export_grid=64, export_offsets=None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_offsets is NULL" in msg
     st, msg = _prefill(num_export=-1, export_grid=64)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_export_states" in msg
-    st, msg = _prefill(export_grid=1088)          # lcm(64, 1088) = 1088 is accepted; the workspace is not
-    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0" in msg
-    st, msg = _prefill()
-    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0 is smaller" in msg
+    st, msg = _prefill(export_grid=1088)          # lcm(64, 1088) = 1088 is accepted; the NULL init_slot is not
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "init_slot is NULL" in msg
     st, msg = _prefill(num_seqs=0, q=None, cu=None)   # no sequences: a no-op
     assert st == B.GDN_OK
-
-
-@pytest.mark.parametrize("entry", ["gdn_chunk_prefill_transform", "gdn_chunk_prefill_scan"])
-def test_prefill_stage_validation(entry):
-    fn = getattr(B.library(), entry)
-    shape = B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
-    st = fn(ctypes.byref(shape), 2, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None,
-            1056, FAKE, FAKE, 0, FAKE, 0, None)
-    assert st == B.GDN_ERR_INVALID_ARGUMENT and "chunk size 64" in B.gdn_last_error()
-    st = fn(ctypes.byref(shape), 2, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None,
-            0, None, None, 0, FAKE, 0, None)
-    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace_bytes 0" in B.gdn_last_error()
 
 
 def test_mixed_step_validation():
@@ -143,14 +128,14 @@ def test_mixed_step_validation():
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, None, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, 0, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "slot_out is NULL" in B.gdn_last_error()
-    # prefill part: export grid off the chunk grid
+    # prefill part: export grid off the chunk grid (init_slot NULL as the guard)
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, FAKE, FAKE, None, 100, FAKE, FAKE, 1, FAKE, 0, None)
+                            FAKE, FAKE, 8, None, FAKE, None, 100, FAKE, FAKE, 1, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_grid 100" in B.gdn_last_error()
-    # prefill part: workspace too small
+    # prefill part: a NULL init_slot
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, 0, FAKE, 0, None)
-    assert st == B.GDN_ERR_INVALID_ARGUMENT and "workspace" in B.gdn_last_error()
+                            FAKE, FAKE, 8, None, FAKE, None, 0, None, None, 0, FAKE, 0, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "init_slot is NULL" in B.gdn_last_error()
 
 
 def test_binding_checks_tensors_before_calling():

@@ -261,17 +261,19 @@ struct NSplit { static constexpr int value = 2; };   // bf16: hi + lo
 template <>
 struct NSplit<float> { static constexpr int value = 1; };
 
-template <typename E, int DK, int HG>
+template <typename E, int DK, int DV, int HG>
 struct ScanSmem {
     static constexpr int QLD = DK + Pad<E>::value;      // Q and K rows
     static constexpr int ALD = kC + 4;                  // fp32 A / T rows
     static constexpr int TLD = kC + Pad<E>::value;      // T1, T2 rows (operand type)
     static constexpr int PLD = kC + Pad<E>::value;      // P rows
+    static constexpr int VLD = DV + Pad<E>::value;      // V rows
     static constexpr int NS = NSplit<E>::value;
     E q[kC * QLD];
     E k[kC * QLD];
     struct Head {
         union {
+            E v[kC * VLD];        // V rows (staging to phase 1)
             float a[kC * ALD];    // A, then T in place (phases 2-4)
             E p[kC * PLD];        // then P (phase 5)
         };
@@ -312,6 +314,15 @@ __device__ __forceinline__ typename Mma<E>::pair row_pair_fromc(const E* hi, con
     return p;
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load (its release fence drains vmcnt), which would expose the
+// latency of the next chunk's prefetch at the first barrier after it is issued.  The
+// scan shares data between waves only through LDS, so waiting for LDS operations is
+// enough; the memory clobber keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // smallest k index that step ks of each order covers
 template <typename M>
 __device__ __forceinline__ int kmin_nat(int ks) { return ks * M::KSTEP; }
@@ -323,7 +334,7 @@ __device__ __forceinline__ int kmin_fromc(int ks) { return M::KSTEP == 32 ? 32 *
 template <typename E, int DK, int DV, int HG>
 __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
     using M = Mma<E>;
-    using SM = ScanSmem<E, DK, HG>;
+    using SM = ScanSmem<E, DK, DV, HG>;
     constexpr int NWH = DV / 32;             // waves per value head
     constexpr int NW = HG * NWH;             // waves
     constexpr int NT = NW * 64;              // threads
@@ -333,9 +344,12 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
     constexpr int VN = Vec<E>::N;            // elements per 16-byte vector
     constexpr int VPR = DK / VN;             // 16-byte vectors per Q/K row
     constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
+    constexpr int VPRV = DV / VN;            // 16-byte vectors per V row
+    constexpr int NPV = HG * kC * VPRV / NT; // prefetched V vectors per thread
     constexpr int TPW = (16 + NW - 1) / NW;  // 16x16 tiles of a 64x64 matrix per wave
     constexpr int NVF = KS_C * 2;            // V fragments per wave
     static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
+    static_assert(NPV * NT == HG * kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
 
     const int G = a.H_v / a.H_k;
@@ -384,9 +398,10 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
     const E* vg = static_cast<const E*>(a.v);
     E* og = static_cast<E*>(a.o);
 
-    // ---- prefetch registers: Q/K row vectors, this wave's V fragments, g/beta
+    // ---- prefetch registers: Q/K row vectors, V row vectors, g/beta (16-byte vector
+    //      loads that nothing consumes until the next chunk is staged)
     uint4 pf[NPF];
-    typename M::frag vpf[NVF];
+    uint4 pv[NPV];
     float gbpf = 0.f;
     auto chunk_bounds = [&](int c, int& tok, int& L, int& e0) {
         const int b0 = c * kC - off64 < 0 ? 0 : c * kC - off64;
@@ -394,51 +409,51 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
         tok = lo + b0;
         L = e0 - b0;
     };
-    auto prefetch = [&](int c, int li, int g4) {
+    // load 16 bytes at a uniform base plus an unsigned 32-bit byte offset (the
+    // scalar-base + vector-offset form of the global load)
+    auto ld16 = [](const void* base, uint32_t off) {
+        return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+    };
+    auto prefetch = [&](int c, int t) {
         int tok, L, e0;
         chunk_bounds(c, tok, L, e0);
+        const E* qb = qg + (size_t)tok * a.H_k * DK;
+        const E* kb = kg + (size_t)tok * a.H_k * DK;
+        const E* vb = vg + (size_t)tok * a.H_v * DV;
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
-            const int i = tid + NT * j;
+            const int i = t + NT * j;
             const int which = i / (kC * VPR);            // 0: Q, 1: K
             const int r = (i / VPR) % kC, vi = i % VPR;
-            const E* src = which == 0 ? qg : kg;
-            pf[j] = r < L ? *reinterpret_cast<const uint4*>(src + ((size_t)(tok + r) * a.H_k + kh) * DK + vi * VN)
-                          : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t off = (uint32_t)((r * a.H_k + kh) * DK + vi * VN) * (uint32_t)sizeof(E);
+            pf[j] = r < L ? ld16(which == 0 ? qb : kb, off) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int kk = 0; kk < KS_C; ++kk)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                typename M::frag f;
-                if constexpr (M::KSTEP == 32) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s = M::nat(kk, g4, e);
-                        f[e] = s < L ? vg[((size_t)(tok + s) * a.H_v + h) * DV + col0 + 16 * nt + li] : (E)0.f;
-                    }
-                } else {
-                    const int s = M::nat(kk, g4, 0);
-                    f = s < L ? vg[((size_t)(tok + s) * a.H_v + h) * DV + col0 + 16 * nt + li] : (E)0.f;
-                }
-                vpf[kk * 2 + nt] = f;
-            }
-        if (tid < 2 * kC * HG) {                          // g then beta for each head
-            const int hx = tid / (2 * kC), which = (tid / kC) & 1, s = tid % kC;
-            const float* src = which == 0 ? a.g : a.beta;
-            gbpf = s < L ? src[(size_t)(tok + s) * a.H_v + h0 + hx] : 0.f;
+        for (int j = 0; j < NPV; ++j) {
+            const int i = t + NT * j;
+            const int hx = i / (kC * VPRV);
+            const int r = (i / VPRV) % kC, vi = i % VPRV;
+            const uint32_t off = (uint32_t)((r * a.H_v + h0 + hx) * DV + vi * VN) * (uint32_t)sizeof(E);
+            pv[j] = r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (t < 2 * kC * HG) {                            // g then beta for each head
+            const int hx = t / (2 * kC), which = (t / kC) & 1, s = t % kC;
+            const float* src = (which == 0 ? a.g : a.beta) + (size_t)tok * a.H_v;
+            const uint32_t off = (uint32_t)(s * a.H_v + h0 + hx) * 4u;
+            gbpf = s < L ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(src) + off) : 0.f;
         }
     };
-    if (nchunks > 0) prefetch(0, lane & 15, lane >> 4);
+    if (nchunks > 0) prefetch(0, tid);
 
     for (int c = 0; c < nchunks; ++c) {
         int tok, L, e0;
         chunk_bounds(c, tok, L, e0);
         // Keep lane-derived addresses inside the loop: without this the compiler hoists
         // every unrolled access's address out of the chunk loop and runs out of registers.
-        asm volatile("" : "+v"(lane));
+        int tid_l = tid;
+        asm volatile("" : "+v"(lane), "+v"(tid_l));
         const int li = lane & 15, g4 = lane >> 4;
-        __syncthreads();   // the previous chunk is done with LDS
+        lds_barrier();   // the previous chunk is done with LDS
 
         // ---- stage this chunk's inputs; prefetch the next chunk
 #pragma unroll
@@ -449,16 +464,28 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
             E* dst = (which == 0 ? sm.q : sm.k) + r * SM::QLD + vi * VN;
             *reinterpret_cast<uint4*>(dst) = pf[j];
         }
-        typename M::frag vcur[NVF];
 #pragma unroll
-        for (int j = 0; j < NVF; ++j) vcur[j] = vpf[j];
+        for (int j = 0; j < NPV; ++j) {
+            const int i = tid + NT * j;
+            const int hx = i / (kC * VPRV);
+            const int r = (i / VPRV) % kC, vi = i % VPRV;
+            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * VN) = pv[j];
+        }
         if (tid < 2 * kC * HG) {
             const int hx = tid / (2 * kC), which = (tid / kC) & 1, s = tid % kC;
             (which == 0 ? sm.hd[hx].graw : sm.hd[hx].braw)[s] = gbpf;
         }
-        __syncthreads();
+        lds_barrier();
+        // the staged inputs are in LDS: fetch the next chunk's behind this chunk's compute
+        if (c + 1 < nchunks) prefetch(c + 1, tid_l);
 
-        // ---- phase 1: gates; K K^T lower tiles
+        // ---- phase 1: this wave's V fragments; gates; K K^T lower tiles
+        typename M::frag vcur[NVF];
+#pragma unroll
+        for (int kk = 0; kk < KS_C; ++kk)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                vcur[kk * 2 + nt] = M::col_nat(hd.v, SM::VLD, col0 + 16 * nt + li, kk, g4);
         if (wv - hh * NWH == 0) {                          // first wave of each head
             const float gs = hd.graw[lane];
             const float bs = hd.braw[lane];
@@ -485,7 +512,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
             }
             kkt[j] = ak;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 2: A for every head (zeros on and above the diagonal)
 #pragma unroll
@@ -506,7 +533,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 3: T = (I + A)^-1 in place, one wave per head
         if (wv - hh * NWH == 0) {
@@ -554,7 +581,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 4: T1 = T diag(beta) and -T2 = -T diag(beta gamma), split, all threads
 #pragma unroll
@@ -572,7 +599,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 5a: P for every head (into the dead A/T space); Z = K S; U = T1 V + (-T2) Z
 #pragma unroll
@@ -598,6 +625,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 Uacc[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -611,43 +639,39 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 Uacc[mt][1] = M::mma_sa(ta, vcur[kk * 2 + 1], Uacc[mt][1]);
             }
         }
-        {
-            f32x4 Zacc[4][2];
+        // Z = K S and U += (-T2) Z, one 16-column tile at a time
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) Zacc[mt][0] = Zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2; ++nt) {
+            __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
+            f32x4 Zacc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Zacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk) {
-                const typename M::frag sb0 = M::acc_fromc(&Sacc[0][0], kk, 2);
-                const typename M::frag sb1 = M::acc_fromc(&Sacc[0][1], kk, 2);
+                const typename M::frag sb = M::acc_fromc(&Sacc[0][nt], kk, 2);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const typename M::frag ka = M::row_fromc(sm.k + (16 * mt + li) * SM::QLD, kk, g4);
-                    Zacc[mt][0] = M::mma(ka, sb0, Zacc[mt][0]);
-                    Zacc[mt][1] = M::mma(ka, sb1, Zacc[mt][1]);
-                }
+                for (int mt = 0; mt < 4; ++mt)
+                    Zacc[mt] = M::mma(M::row_fromc(sm.k + (16 * mt + li) * SM::QLD, kk, g4), sb, Zacc[mt]);
             }
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
-                const typename M::frag zb0 = M::acc_fromc(&Zacc[0][0], kk, 2);
-                const typename M::frag zb1 = M::acc_fromc(&Zacc[0][1], kk, 2);
+                const typename M::frag zb = M::acc_fromc(&Zacc[0], kk, 1);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (kmin_fromc<M>(kk) > 16 * mt + 15) continue;
                     const typename M::pair ta = row_pair_fromc<E>(hd.t2[0] + (16 * mt + li) * SM::TLD,
                                                                   hd.t2[SM::NS - 1] + (16 * mt + li) * SM::TLD, kk, g4);
-                    Uacc[mt][0] = M::mma_sa(ta, zb0, Uacc[mt][0]);
-                    Uacc[mt][1] = M::mma_sa(ta, zb1, Uacc[mt][1]);
+                    Uacc[mt][nt] = M::mma_sa(ta, zb, Uacc[mt][nt]);
                 }
             }
         }
-        // this chunk's inputs are consumed: fetch the next chunk's while the rest runs
-        if (c + 1 < nchunks) prefetch(c + 1, li, g4);
-        __syncthreads();   // P is complete
+        lds_barrier();   // P is complete
 
         // ---- phase 5b: O = gamma o (Q S) + P U, one 16-column tile at a time
         const float* gam = hd.gate + GATE_GAM * kC;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 Oacc[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -681,6 +705,7 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
                 }
         }
 
+        __builtin_amdgcn_sched_barrier(0);
         // ---- phase 5c: S = gamma_last S + K^T (diag(e^(G_last - G)) U)
         const float gl_last = gam[kC - 1];
         const float* kdec = hd.gate + GATE_KDEC * kC;

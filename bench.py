@@ -17,8 +17,8 @@ kernel's roofline; and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
 """
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -32,6 +32,7 @@ METRIC = "GDN prefill tokens/s + decode state GB/s (frac of HBM peak) on 1 MI355
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 CHUNK = 64
+KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "scan_kernel": "gdn_prefill.hip"}
 
 
 def parse():
@@ -48,10 +49,39 @@ def parse():
     return ap.parse_args()
 
 
+def source_digest(kernel):
+    """sha256 of the HIP source a kernel is built from; hardware byte counters taken
+    on another version of the source no longer describe the kernel."""
+    path = os.path.join(ROOT, "gated_deltanet_rule_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter profile (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a copy of known size), or
+    None when there is none for the current source of the kernel."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def algorithmic_flops_per_token(H_k, H_v, d_k, d_v, C=CHUNK):
     """Flops per prefill token of the chunked form, triangles counted once, K K^T and
     Q K^T once per key head: H_k 2 C d_k + H_v (C (d_k + d_v) + C d_v + 6 d_k d_v)."""
     return H_k * 2 * C * d_k + H_v * (C * (d_k + d_v) + C * d_v + 6 * d_k * d_v)
+
+
+def algorithmic_bytes_per_token(H_k, H_v, d_k, d_v, elem):
+    """HBM bytes every prefill token must move: q and k (H_k d_k each), v and o (H_v
+    d_v each) at elem bytes per element, and the fp32 g and beta of every value head."""
+    return 2 * H_k * d_k * elem + 2 * H_v * d_v * elem + 8 * H_v
 
 
 def main():
@@ -78,6 +108,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy_gbps = copy_bandwidth(torch, dev)
     t_gen = time.time()
     wd = W.config(1)                                           # decode batch
     wp = W.config(4, fill_pool=False)                          # long prefill
@@ -164,18 +195,26 @@ def main():
     f_tok = algorithmic_flops_per_token(H_k, H_v, d_k, d_v)
     pre_flops = f_tok * Tp
     pre_tflops = pre_flops / (t_pre * 1e-3) / 1e12
+    state_bytes = 4 * H_v * d_k * d_v
+    b_tok = algorithmic_bytes_per_token(H_k, H_v, d_k, d_v, 2)
+    pre_bytes = b_tok * Tp + state_bytes * (offs[-1] + N)  # activations + exports + final states
+    pre_gbps = pre_bytes / (t_pre * 1e-3) / 1e9
     kernels = {
         "decode_kernel": {"ms": round(t_dec, 5), "bound": "hbm", "achieved": round(dec_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                          "bytes_per_launch": dec_bytes},
-        "scan_kernel": {"ms": round(t_pre, 4), "bound": "mfma", "achieved": round(pre_tflops, 2),
-                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                          "bytes_per_launch": dec_bytes, "traffic": measured_traffic("decode_kernel")},
+        # arithmetic intensity pre_flops / pre_bytes (about 156 flop/B) is below the bf16
+        # ridge (2500 / 8 = 312 flop/B): HBM binds, MFMA use is reported beside it
+        "scan_kernel": {"ms": round(t_pre, 4), "bound": "hbm", "achieved": round(pre_gbps, 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+                        "bytes_per_launch": pre_bytes, "traffic": measured_traffic("scan_kernel"),
+                        "mfma_tflops": round(pre_tflops, 2), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                         "flops_per_launch": pre_flops},
     }
     dominant = "scan_kernel" if t_pre >= t_dec else "decode_kernel"
     roof = kernels[dominant]
     roofline = {"kernel": dominant, "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"],
-                "unit": roof["unit"], "frac": roof["frac"], "traffic": None}
+                "unit": roof["unit"], "frac": roof["frac"], "traffic": roof["traffic"]}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -189,7 +228,10 @@ def main():
         "decode": {"state_GB_per_s": round(dec_gbps, 1), "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "ms": round(t_dec, 5), "state_bytes": dec_bytes},
         "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": round(t_pre, 4),
-                    "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok},
+                    "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+                    "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok,
+                    "bytes_per_token": b_tok},
+        "copy_GB_per_s": round(copy_gbps, 1),
         "roofline": roofline,
         "kernels": kernels,
     }
@@ -199,6 +241,25 @@ def main():
     print("input generation %.1f s; step %.3f ms = decode %.4f + prefill %.4f ms" % (
         gen_s, ms_step, t_dec, t_pre), file=sys.stderr)
     print(json.dumps(out), flush=True)
+
+
+def copy_bandwidth(torch, dev, mib=1024, reps=10):
+    """Achievable HBM bandwidth of a plain device-to-device copy (read + write bytes
+    per second), the practical ceiling next to the 8 TB/s peak."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
 
 
 def cpu_baseline(wp, wd, n_seqs):

@@ -194,6 +194,8 @@ def _prefill_common(dev, num_seqs, cu_seqlens, init_slot, final_slot, start_pos,
             if tuple(export_states.shape[1:]) != (H_v, d_k, d_v):
                 raise ValueError("export_states must be [E, %d, %d, %d]" % (H_v, d_k, d_v))
             n_exp = export_states.shape[0]
+    if workspace is None:            # the library reports an error if the call needs one
+        return n_exp, 0
     _need(workspace, "workspace", device=dev)
     return n_exp, workspace.numel() * workspace.element_size()
 
@@ -216,7 +218,7 @@ def _prefill_call(entry, q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot,
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot, *,
-                      scale: float, workspace, start_pos=None, export_grid: int = 0,
+                      scale: float, workspace=None, start_pos=None, export_grid: int = 0,
                       export_states=None, export_offsets=None, stream=None) -> None:
     """Chunked prefill over len(cu_seqlens) - 1 packed sequences (see include/gdn.h)."""
     _prefill_call("gdn_chunk_prefill", q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot,
@@ -224,7 +226,7 @@ def gdn_chunk_prefill(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, fi
 
 
 def gdn_mixed_step(q, k, v, g, beta, o, state_pool, slot_in, slot_out, cu_seqlens_prefill, init_slot,
-                   final_slot, *, scale: float, workspace, start_pos=None, export_grid: int = 0,
+                   final_slot, *, scale: float, workspace=None, start_pos=None, export_grid: int = 0,
                    export_states=None, export_offsets=None, stream=None) -> None:
     """One mixed step: rows [0, len(slot_in)) decode, the rest prefill (see include/gdn.h)."""
     T = q.shape[0]

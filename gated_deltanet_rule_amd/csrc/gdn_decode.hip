@@ -1,6 +1,6 @@
 // gdn_decode.hip -- packed single-token recurrent decode for gfx950 (MI355X).
 //
-// One workgroup of 256 threads advances the state of one (row, value head) by one
+// One workgroup of 1024 threads advances the state of one (row, value head) by one
 // token ("[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
 // sections "Why" and "How": cached rows take the packed recurrent decode path).
 // The work is bound by HBM: each state (d_k x d_v fp32, 64 KiB at d = 128) is read
@@ -10,8 +10,11 @@
 //     S <- exp(g) S;   u = beta (v - S^T k);   S <- S + k u^T;   o = scale S^T q
 //
 // Thread layout: a state row (d_v floats) is covered by d_v/4 threads holding one
-// float4 each; the 256 threads form 256/(d_v/4) row groups, and row group r holds
-// rows r, r + RG, r + 2 RG, ...  The two reductions over d_k (S^T k and S^T q) are
+// float4 each; the 1024 threads form 1024/(d_v/4) row groups, and row group r holds
+// rows r, r + RG, r + 2 RG, ...  Large workgroups keep few state rows per thread, so
+// two workgroups fit on a compute unit and the later ones' loads overlap the earlier
+// ones' stores (a cold in-place update of 64 KiB states runs at the speed of a plain
+// read-modify-write of the same blocks).  The two reductions over d_k (S^T k and S^T q) are
 // per-thread partial sums followed by a fixed-order sum over the row groups through
 // LDS, so the result does not depend on anything but the row's own data: a row's
 // output and state are bitwise the same in any batch, at any position.
@@ -62,7 +65,7 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float4 v) {
     *reinterpret_cast<bf16x4*>(p) = x;
 }
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 // State traffic is touched once per call: stream it with non-temporal loads and
 // stores so it neither evicts nor waits on cache lines other work could reuse.

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_prefill_bf16.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ALU ops are switched off for every device pass (the hipcc host pass

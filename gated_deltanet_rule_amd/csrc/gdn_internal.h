@@ -1,5 +1,5 @@
 // gdn_internal.h -- launcher interface between the C ABI layer (gdn_api.cpp) and the
-// gfx950 kernels (gdn_decode.hip, gdn_prefill.hip).  Host-side declarations only.
+// gfx950 kernels (gdn_decode.hip, gdn_prefill.hip, gdn_prefill_bf16.hip).  Host-side declarations only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,5 +58,7 @@ size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_t
 // Value heads that share one workgroup (and its staged Q and K).
 int prefill_heads_per_group(int dtype, int H_k, int H_v);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The bf16 kernel (gdn_prefill_bf16.hip); launch_prefill routes bf16 calls to it.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

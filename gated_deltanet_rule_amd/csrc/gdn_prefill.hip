@@ -790,10 +790,7 @@ int prefill_heads_per_group(int dtype, int H_k, int H_v) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    if (a.dtype == 1) {
-        if (prefill_heads_per_group(a.dtype, a.H_k, a.H_v) == 2) return launch_dims<__bf16, 2>(a, stream);
-        return launch_dims<__bf16, 1>(a, stream);
-    }
+    if (a.dtype == 1) return launch_prefill_bf16(a, stream);
     return launch_dims<float, 1>(a, stream);
 }
 

@@ -1,0 +1,566 @@
+// gdn_prefill_bf16.hip -- chunked prefill of the gated delta rule for bf16 inputs on
+// gfx950 (MI355X).
+//
+// Defined by: "[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
+// section "Why" (fresh prefill rows go through a 64-token chunk prefill);
+// "[V1][Hybrid] GatedDeltaNet Automatic Prefix Caching", section "Purpose" (states at
+// chunk boundaries returned as one flat stream); "[WIP][Kernel] Enable GDN
+// batch-invariant prefix caching", section "Purpose" (one lcm(64, block) grid).
+//
+// Within a chunk of L <= 64 tokens (rows r, s) with start state S (d_k x d_v) the
+// token recurrence S <- e^g (I - beta k k^T) S + beta k v^T is evaluated in its
+// chunked form:
+//     G   = inclusive cumsum of g inside the chunk,  gamma = e^G,  D[r][s] = e^(G_r - G_s)
+//     A   = strictly lower part of diag(beta) (K K^T) o D
+//     R   = diag(beta) (V - diag(gamma) K S)
+//     U   = (I + A)^-1 R                         (a unit lower-triangular solve)
+//     O   = scale (diag(gamma) Q S + (Q K^T o D o lower-incl-diagonal) U)
+//     S  <- gamma_last S + K^T (diag(e^(G_last - G)) U)
+//
+// One workgroup owns one sequence and HG value heads that share a key head, and walks
+// the sequence's chunks in order.  Per value head, d_v is split into 32-column strips,
+// one wave each; a wave keeps its strip of S (d_k x 32, fp32) in MFMA accumulators
+// for the whole sequence.  The d_v columns of S, R, U and O are independent, so
+// strips never exchange data.  The solve runs on 16-row blocks of the chunk:
+//     U_i = T_ii (R_i - sum_{j<i} A_ij U_j),   T_ii = (I + A_ii)^-1 (16 x 16)
+// Per chunk, with three workgroup barriers:
+//   stage    the previous chunk's prefetched Q, K (also transposed) and V rows go to
+//            LDS; the first wave of each head scans the gates from its registers
+//   phase 1  lower 16x16 tiles of K K^T and Q K^T (shared by the HG heads), turned
+//            into -A_ij blocks, fp32 A_ii blocks and P blocks per head; then, per
+//            strip, Z = K S and Q S on MFMA and R = beta (V - gamma Z), V entering
+//            the accumulators through an identity product
+//   phase 2  the first wave of each head inverts the four A_ii blocks by forward
+//            substitution (lane 16b + j owns column j of block b)
+//   phase 3  per strip: the block solve for U, each output row block as soon as
+//            its U blocks exist, then the state update and the grid export
+// Precision.  All products are bf16 MFMA with fp32 accumulation.  q, k and v enter
+// exactly; S, Z and P enter as single bf16 values; every operand the solve and the
+// state update depend on -- the -A_ij and T_ii blocks, the right-hand sides, U and
+// the decayed U -- enters as a hi + lo pair of bf16 values (x = hi + lo to about
+// 2^-17) in three products (hi hi, hi lo, lo hi) or two when the other side is
+// exact.  Gates, the A_ii inverses and all accumulators are fp32.  A sequence's work
+// never depends on the other sequences of the call, so its results are bitwise
+// independent of its batch-mates; chunks lie on the absolute 64-token grid, so a
+// resume from an exported grid state continues with the same arithmetic.
+#include <hip/hip_runtime.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+using dev::kC;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- MFMA operands
+//
+// 16x16 output tiles: the C/D tile sits in lane l as C[4 (l / 16) + i][l % 16],
+// i = 0..3.  16x16x32: lane l holds A[l % 16][k] and B[k][l % 16] for eight k; the
+// "natural" order gives lane group g the k = 8g..8g+7, the "from-C" order gives it
+// k = 4g..4g+3 and 16+4g..16+4g+3, the rows a pair of C tiles already holds in a
+// lane.  16x16x16: lane group g holds k = 4g..4g+3, which is exactly the rows one C
+// tile holds, so a C tile converted to bf16 is a B operand as it stands.
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                     c, 0, 0, 0);
+}
+
+struct Split4 { bf16x4 hi, lo; };
+
+// x = hi + lo: hi rounded to bf16, lo the exact remainder rounded once
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        s.hi[e] = h;
+        s.lo[e] = (__bf16)(x[e] - (float)h);
+    }
+    return s;
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void st4(__bf16* p, bf16x4 x) { *reinterpret_cast<bf16x4*>(p) = x; }
+
+// 16x32 operand of a row-major LDS row, k from 32 ks in from-C order
+__device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g) {
+    return cat8(ld4(row + 32 * ks + 4 * g), ld4(row + 32 * ks + 16 + 4 * g));
+}
+
+// B operand (from-C order, k step ks) out of a pair of state accumulator tiles
+__device__ __forceinline__ bf16x8 state_frag(const f32x4& t0, const f32x4& t1) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (__bf16)t0[i];
+        r[4 + i] = (__bf16)t1[i];
+    }
+    return r;
+}
+
+// Lower 16x16 blocks (i, j), j <= i, of a 64x64 matrix, numbered row by row.
+__device__ __forceinline__ constexpr int blk(int i, int j) { return i * (i + 1) / 2 + j; }
+
+enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, kGates = 4 };
+
+template <int DK, int DV, int HG>
+struct Smem {
+    static constexpr int QLD = DK + 8;        // Q and K rows (bf16)
+    static constexpr int KTLD = kC + 8;       // K^T rows (bf16)
+    static constexpr int VLD = DV + 8;        // V rows (bf16)
+    static constexpr int BLD = 20;            // rows of a 16x16 bf16 block
+    static constexpr int BSZ = 16 * BLD;
+    static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
+    static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
+    __bf16 q[kC * QLD];
+    __bf16 k[kC * QLD];
+    __bf16 kt[2][DK * KTLD];                  // K^T, by chunk parity (the state update of
+                                              // chunk c reads it while chunk c+1 is staged)
+    struct Head {
+        __bf16 v[kC * VLD];
+        __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
+        __bf16 p[10][BSZ];                    // P blocks
+        float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
+        float gate[2][kGates * kC];           // by chunk parity
+    } hd[HG];
+};
+
+// Tile tt of phase 1: 0..9 the lower blocks of K K^T, 10..19 those of Q K^T.
+__device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
+    i = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+    j = t - i * (i + 1) / 2;
+}
+
+template <int DK, int DV, int HG>
+__global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
+    using SM = Smem<DK, DV, HG>;
+    constexpr int NWH = DV / 32;             // waves per value head
+    constexpr int NW = HG * NWH;             // waves
+    constexpr int NT = NW * 64;              // threads
+    constexpr int MT_S = DK / 16;            // 16-row tiles of the state
+    constexpr int KS_DK = DK / 32;           // 32-wide k steps over d_k
+    constexpr int VPR = DK / 8;              // 16-byte vectors per Q/K row
+    constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
+    constexpr int VPRV = DV / 8;             // 16-byte vectors per V row
+    constexpr int NPV = HG * kC * VPRV / NT; // prefetched V vectors per thread
+    static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
+    static_assert(NPV * NT == HG * kC * VPRV, "V prefetch must divide evenly");
+    __shared__ __attribute__((aligned(16))) SM sm;
+
+    const int G = a.H_v / a.H_k;
+    const int GG = G / HG;
+    const int seq = blockIdx.x / (a.H_k * GG);
+    const int rem = blockIdx.x - seq * (a.H_k * GG);
+    const int kh = rem / GG;
+    const int h0 = kh * G + (rem - kh * GG) * HG;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    int lane = tid & 63;
+    const int hh = wv / NWH;                 // this wave's head within the group
+    const int h = h0 + hh;
+    const int col0 = 32 * (wv - hh * NWH);
+    const bool lead = wv == hh * NWH;        // first wave of its head
+    typename SM::Head& hd = sm.hd[hh];
+
+    const size_t SE = (size_t)DK * DV;
+    // state strip: Sacc[mt][nt] holds S[16 mt + 4 g + i][col0 + 16 nt + li]
+    f32x4 Sacc[MT_S][2];
+    const int isl = a.init_slot ? a.init_slot[seq] : -1;
+    if (isl >= 0 && isl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
+        const float* src = a.pool + ((size_t)isl * a.H_v + h) * SE;
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Sacc[mt][nt][i] = src[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int lo, len;
+    dev::seq_range(a.cu_seqlens, seq, a.total_tokens, lo, len);
+    const int64_t pos0 = a.start_pos ? a.start_pos[seq] : 0;
+    const int off64 = (int)(pos0 & (kC - 1));
+    const int nchunks = dev::seq_chunks(len, off64);
+
+    const __bf16* qg = static_cast<const __bf16*>(a.q);
+    const __bf16* kg = static_cast<const __bf16*>(a.k);
+    const __bf16* vg = static_cast<const __bf16*>(a.v);
+    __bf16* og = static_cast<__bf16*>(a.o);
+
+    // identity B operand of the 16x16x16 product: B[4 g + e][n] = (4 g + e == n)
+    bf16x4 ident;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ident[e] = (__bf16)((4 * (lane >> 4) + e == (lane & 15)) ? 1.f : 0.f);
+
+    // ---- prefetch registers: Q/K row vectors, V row vectors, and (first wave of each
+    //      head) this head's g and beta, one token per lane
+    uint4 pf[NPF];
+    uint4 pv[NPV];
+    float gpf = 0.f, bpf = 0.f;
+    auto ld16 = [](const void* base, uint32_t off) {
+        return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+    };
+    auto prefetch = [&](int c, int t) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const __bf16* qb = qg + (size_t)tok * a.H_k * DK;
+        const __bf16* kb = kg + (size_t)tok * a.H_k * DK;
+        const __bf16* vb = vg + (size_t)tok * a.H_v * DV;
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int i = t + NT * j;
+            const int which = i / (kC * VPR);            // 0: Q, 1: K
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            const uint32_t off = (uint32_t)((r * a.H_k + kh) * DK + vi * 8) * 2u;
+            pf[j] = r < L ? ld16(which == 0 ? qb : kb, off) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const int i = t + NT * j;
+            const int hx = i / (kC * VPRV);
+            const int r = (i / VPRV) % kC, vi = i % VPRV;
+            const uint32_t off = (uint32_t)((r * a.H_v + h0 + hx) * DV + vi * 8) * 2u;
+            pv[j] = r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (lead) {
+            const int s = t & 63;
+            const uint32_t off = (uint32_t)(s * a.H_v + h) * 4u;
+            const char* gb = reinterpret_cast<const char*>(a.g + (size_t)tok * a.H_v);
+            const char* bb = reinterpret_cast<const char*>(a.beta + (size_t)tok * a.H_v);
+            gpf = s < L ? *reinterpret_cast<const float*>(gb + off) : 0.f;
+            bpf = s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
+        }
+    };
+    if (nchunks > 0) prefetch(0, tid);
+
+    for (int c = 0; c < nchunks; ++c) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const int buf = c & 1;
+        // Keep lane-derived addresses inside the loop: without this the compiler hoists
+        // every unrolled access's address out of the chunk loop and runs out of registers.
+        int tid_l = tid;
+        asm volatile("" : "+v"(lane), "+v"(tid_l));
+        const int li = lane & 15, g4 = lane >> 4;
+
+        // ---- stage this chunk's inputs.  No barrier is needed before: Q, K and V were
+        //      last read in phase 1 of the previous chunk, K^T and the gates go to the
+        //      other parity, and the blocks phase 1 writes are protected by the barrier
+        //      after staging.
+        __bf16* kt = sm.kt[buf];
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int i = tid_l + NT * j;
+            const int which = i / (kC * VPR);
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            *reinterpret_cast<uint4*>((which == 0 ? sm.q : sm.k) + r * SM::QLD + vi * 8) = pf[j];
+            if (which == 1) {
+                const bf16x8 x = __builtin_bit_cast(bf16x8, pf[j]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + r] = x[e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const int i = tid_l + NT * j;
+            const int hx = i / (kC * VPRV);
+            const int r = (i / VPRV) % kC, vi = i % VPRV;
+            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
+        }
+        if (lead) {                          // gates of this head, lane = token
+            constexpr float kLog2e = 1.4426950408889634f;
+            const float G2 = dev::wave_inclusive_sum(gpf * kLog2e, lane);
+            const float G2_last = __shfl(G2, kC - 1, 64);
+            float* gt = hd.gate[buf];
+            gt[GATE_G2 * kC + lane] = G2;
+            gt[GATE_GAM * kC + lane] = exp2f(G2);
+            gt[GATE_BET * kC + lane] = bpf;
+            gt[GATE_KDEC * kC + lane] = exp2f(G2_last - G2);
+        }
+        dev::lds_barrier();
+        // the staged inputs are in LDS: fetch the next chunk's behind this chunk's compute
+        if (c + 1 < nchunks) prefetch(c + 1, tid_l);
+
+        // ---- phase 1a: lower tiles of K K^T and Q K^T -> -A_ij, A_ii^T, P per head
+        for (int tt = wv; tt < 20; tt += NW) {
+            int i, j;
+            tile_ij(tt % 10, i, j);
+            const __bf16* X = tt < 10 ? sm.k : sm.q;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS_DK; ++kk)
+                acc = mma32(ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4),
+                            ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4), acc);
+            // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
+            const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
+#pragma unroll
+            for (int x = 0; x < HG; ++x) {
+                typename SM::Head& hx = sm.hd[x];
+                const float* gt = hx.gate[buf];
+                const float G2r = gt[GATE_G2 * kC + r];
+                const f32x4 G2s = *reinterpret_cast<const f32x4*>(gt + GATE_G2 * kC + s0);
+                if (tt < 10) {
+                    const float br = gt[GATE_BET * kC + r];
+                    f32x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        val[e] = s0 + e < r ? br * acc[e] * exp2f(G2r - G2s[e]) : 0.f;
+                    if (i == j) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hx.at[i * SM::ATB + (4 * g4 + e) * SM::ATLD + li] = val[e];
+                    } else {
+                        const Split4 sp = split4(-val);
+                        st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                        st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                    }
+                } else {
+                    bf16x4 pv4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pv4[e] = (__bf16)(s0 + e <= r ? acc[e] * exp2f(G2r - G2s[e]) : 0.f);
+                    st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
+                }
+            }
+        }
+
+        // ---- phase 1b: Z = K S and Q S for this strip; R = beta (V - gamma Z)
+        const float* gt = hd.gate[buf];
+        f32x4 Racc[4][2], Oacc[4][2];
+        {
+            bf16x8 Sb[KS_DK][2];
+#pragma unroll
+            for (int kk = 0; kk < KS_DK; ++kk)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) Sb[kk][nt] = state_frag(Sacc[2 * kk][nt], Sacc[2 * kk + 1][nt]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    const bf16x8 ak = row_fromc(sm.k + (16 * mt + li) * SM::QLD, kk, g4);
+                    const bf16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        Racc[mt][nt] = mma32(ak, Sb[kk][nt], Racc[mt][nt]);
+                        Oacc[mt][nt] = mma32(aq, Sb[kk][nt], Oacc[mt][nt]);
+                    }
+                }
+            }
+        }
+        const float gam_last = gt[GATE_GAM * kC + kC - 1];
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] *= gam_last;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const f32x4 gam = *reinterpret_cast<const f32x4*>(gt + GATE_GAM * kC + 16 * mt + 4 * g4);
+            const f32x4 bet = *reinterpret_cast<const f32x4*>(gt + GATE_BET * kC + 16 * mt + 4 * g4);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                Oacc[mt][nt] *= gam;
+                // + V through V I, onto -gamma Z
+                const bf16x4 av = ld4(hd.v + (16 * mt + li) * SM::VLD + col0 + 16 * nt + 4 * g4);
+                Racc[mt][nt] = mma16(av, ident, -gam * Racc[mt][nt]);
+                Racc[mt][nt] *= bet;
+            }
+        }
+        dev::lds_barrier();   // A, P and the gates of every head are complete
+
+        // ---- phase 2: T_bb = (I + A_bb)^-1 for the four diagonal blocks, first wave
+        //      of each head; lane 16 b + j computes column j of block b
+        if (lead) {
+            const int b = g4, jc = li;
+            const float* AT = hd.at + b * SM::ATB;
+            float acc[16], t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                t[s] = s < jc ? 0.f : (s == jc ? 1.f : acc[s]);
+                if (s < 15) {
+                    const float* row = AT + s * SM::ATLD;   // row s holds A[r][s] at column r
+#pragma unroll
+                    for (int r4 = (s + 1) / 4; r4 < 4; ++r4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4*>(row + 4 * r4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-av[e], t[s], acc[4 * r4 + e]);
+                    }
+                }
+            }
+            __bf16* th = hd.sol[blk(b, b)][0];
+            __bf16* tl = hd.sol[blk(b, b)][1];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const __bf16 x = (__bf16)t[r];
+                th[r * SM::BLD + jc] = x;
+                tl[r * SM::BLD + jc] = (__bf16)(t[r] - (float)x);
+            }
+        }
+        dev::lds_barrier();   // T_ii blocks are complete
+
+        // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
+        //      U_0..U_i exist; then the state update
+        __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
+        Split4 Us[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 X = Racc[i][nt];
+#pragma unroll
+                for (int j = 0; j < i; ++j) {
+                    const bf16x4 ah = ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4);
+                    const bf16x4 al = ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4);
+                    X = mma16(ah, Us[j][nt].hi, X);
+                    X = mma16(ah, Us[j][nt].lo, X);
+                    X = mma16(al, Us[j][nt].hi, X);
+                }
+                const Split4 xs = split4(X);
+                const bf16x4 th = ld4(hd.sol[blk(i, i)][0] + li * SM::BLD + 4 * g4);
+                const bf16x4 tl = ld4(hd.sol[blk(i, i)][1] + li * SM::BLD + 4 * g4);
+                f32x4 U = mma16(th, xs.hi, f32x4{0.f, 0.f, 0.f, 0.f});
+                U = mma16(th, xs.lo, U);
+                U = mma16(tl, xs.hi, U);
+                Racc[i][nt] = U;
+                Us[i][nt] = split4(U);
+            }
+            // O rows 16 i .. 16 i + 15: + P_i,(0..i) U_(0..i), blocks in pairs
+            const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+#pragma unroll
+            for (int kk = 0; 2 * kk <= i; ++kk) {
+                const int j0 = 2 * kk, j1 = 2 * kk + 1;
+                const bf16x4 p0 = ld4(hd.p[blk(i, j0)] + li * SM::BLD + 4 * g4);
+                const bf16x4 p1 = j1 <= i ? ld4(hd.p[blk(i, j1)] + li * SM::BLD + 4 * g4) : z4;
+                const bf16x8 pa = cat8(p0, p1);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const bf16x4 h1 = j1 <= i ? Us[j1][nt].hi : z4;
+                    const bf16x4 l1 = j1 <= i ? Us[j1][nt].lo : z4;
+                    Oacc[i][nt] = mma32(pa, cat8(Us[j0][nt].hi, h1), Oacc[i][nt]);
+                    Oacc[i][nt] = mma32(pa, cat8(Us[j0][nt].lo, l1), Oacc[i][nt]);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * i + 4 * g4 + e;
+                    const uint32_t off = (uint32_t)(r * a.H_v * DV + 16 * nt + li) * 2u;
+                    if (r < L)
+                        *reinterpret_cast<__bf16*>(reinterpret_cast<char*>(obase) + off) =
+                            (__bf16)(a.scale * Oacc[i][nt][e]);
+                }
+        }
+
+        // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const f32x4 kd0 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 4 * g4);
+            const f32x4 kd1 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 16 + 4 * g4);
+            bf16x8 bh[2], bl[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const Split4 s0 = split4(Racc[2 * kk][nt] * kd0);
+                const Split4 s1 = split4(Racc[2 * kk + 1][nt] * kd1);
+                bh[nt] = cat8(s0.hi, s1.hi);
+                bl[nt] = cat8(s0.lo, s1.lo);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT_S; ++mt) {
+                const bf16x8 ka = row_fromc(kt + (16 * mt + li) * SM::KTLD, kk, g4);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    Sacc[mt][nt] = mma32(ka, bh[nt], Sacc[mt][nt]);
+                    Sacc[mt][nt] = mma32(ka, bl[nt], Sacc[mt][nt]);
+                }
+            }
+        }
+
+        // ---- export on the grid
+        if (a.export_grid > 0) {
+            const int64_t p_end = pos0 + e0;
+            if (p_end % a.export_grid == 0) {
+                const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
+                const int64_t idx = (int64_t)a.export_offsets[seq] + m;
+                if (idx >= 0 && idx < a.export_capacity) {
+                    float* dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+#pragma unroll
+                    for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
+                }
+            }
+        }
+    }
+
+    const int fsl = a.final_slot ? a.final_slot[seq] : -1;
+    if (fsl >= 0 && fsl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
+        float* dst = a.pool + ((size_t)fsl * a.H_v + h) * SE;
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
+    }
+}
+
+template <int DK, int DV, int HG>
+hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
+    const int G = a.H_v / a.H_k;
+    const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG>), dim3(blocks), dim3(HG * DV * 2), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int HG>
+hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, HG>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, HG>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, HG>(a, stream);
+    return launch_typed<64, 64, HG>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    if ((a.H_v / a.H_k) % 2 == 0) return launch_dims<2>(a, stream);
+    return launch_dims<1>(a, stream);
+}
+
+}  // namespace gdn

@@ -134,7 +134,8 @@ struct Smem {
     __bf16 q[kC * QLD];
     __bf16 k[kC * QLD];
     __bf16 kt[2][DK * KTLD];                  // K^T, by chunk parity (the state update of
-                                              // chunk c reads it while chunk c+1 is staged)
+                                              // chunk c reads it while chunk c+1 is staged);
+                                              // row d holds token group q at group q ^ (d / 8)
     struct Head {
         __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
@@ -159,10 +160,11 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
     constexpr int KS_DK = DK / 32;           // 32-wide k steps over d_k
     constexpr int VPR = DK / 8;              // 16-byte vectors per Q/K row
-    constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
+    constexpr int NQ = kC * VPR / NT;        // prefetched Q (and K) vectors per thread
     constexpr int VPRV = DV / 8;             // 16-byte vectors per V row
     constexpr int NPV = HG * kC * VPRV / NT; // prefetched V vectors per thread
-    static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
+    constexpr int NNL = HG * (NWH - 1);      // waves that are not the first of their head
+    static_assert(NQ * NT == kC * VPR, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == HG * kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
 
@@ -220,45 +222,89 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 
     // ---- prefetch registers: Q/K row vectors, V row vectors, and (first wave of each
     //      head) this head's g and beta, one token per lane
-    uint4 pf[NPF];
+    uint4 pq[NQ], pk[NQ];
     uint4 pv[NPV];
     float gpf = 0.f, bpf = 0.f;
     auto ld16 = [](const void* base, uint32_t off) {
         return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
     };
-    auto prefetch = [&](int c, int t) {
+    auto prefetch = [&](int c, unsigned t) {
         int b0, e0;
         dev::chunk_span(c, off64, len, b0, e0);
         const int tok = lo + b0, L = e0 - b0;
-        const __bf16* qb = qg + (size_t)tok * a.H_k * DK;
-        const __bf16* kb = kg + (size_t)tok * a.H_k * DK;
-        const __bf16* vb = vg + (size_t)tok * a.H_v * DV;
+        const __bf16* qb = qg + ((size_t)tok * a.H_k + kh) * DK;
+        const __bf16* kb = kg + ((size_t)tok * a.H_k + kh) * DK;
+        const __bf16* vb = vg + ((size_t)tok * a.H_v + h0) * DV;
 #pragma unroll
-        for (int j = 0; j < NPF; ++j) {
-            const int i = t + NT * j;
-            const int which = i / (kC * VPR);            // 0: Q, 1: K
-            const int r = (i / VPR) % kC, vi = i % VPR;
-            const uint32_t off = (uint32_t)((r * a.H_k + kh) * DK + vi * 8) * 2u;
-            pf[j] = r < L ? ld16(which == 0 ? qb : kb, off) : make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < NQ; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned r = i / VPR, vi = i % VPR;
+            const uint32_t off = (r * (unsigned)a.H_k * DK + vi * 8) * 2u;
+            const bool in = (int)r < L;
+            pq[j] = in ? ld16(qb, off) : make_uint4(0u, 0u, 0u, 0u);
+            pk[j] = in ? ld16(kb, off) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
-            const int i = t + NT * j;
-            const int hx = i / (kC * VPRV);
-            const int r = (i / VPRV) % kC, vi = i % VPRV;
-            const uint32_t off = (uint32_t)((r * a.H_v + h0 + hx) * DV + vi * 8) * 2u;
-            pv[j] = r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
+            const unsigned i = t + NT * j;
+            const unsigned hx = i / (kC * VPRV);
+            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
+            const uint32_t off = ((r * (unsigned)a.H_v + hx) * DV + vi * 8) * 2u;
+            pv[j] = (int)r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
         }
         if (lead) {
-            const int s = t & 63;
-            const uint32_t off = (uint32_t)(s * a.H_v + h) * 4u;
+            const unsigned s = t & 63;
+            const uint32_t off = (s * (unsigned)a.H_v + (unsigned)h) * 4u;
             const char* gb = reinterpret_cast<const char*>(a.g + (size_t)tok * a.H_v);
             const char* bb = reinterpret_cast<const char*>(a.beta + (size_t)tok * a.H_v);
-            gpf = s < L ? *reinterpret_cast<const float*>(gb + off) : 0.f;
-            bpf = s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
+            gpf = (int)s < L ? *reinterpret_cast<const float*>(gb + off) : 0.f;
+            bpf = (int)s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
         }
     };
-    if (nchunks > 0) prefetch(0, tid);
+    // Write chunk c's prefetched inputs to LDS: Q, K and V rows, K^T and the gates
+    // (those two by chunk parity).  Runs before the loop for chunk 0 and, for chunk
+    // c + 1, right after the barrier that ends phase 2 of chunk c: Q, K and V were
+    // last read in phase 1, and the other parity of K^T and the gates was last read
+    // in phase 3 of chunk c - 1.  Doing it before phase 3 issues its stores also
+    // keeps the wait for the prefetch loads from waiting for those stores.
+    auto stage = [&](int c, unsigned t) {
+        const int buf = c & 1;
+        __bf16* kt = sm.kt[buf];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned r = i / VPR, vi = i % VPR;
+            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + vi * 8) = pq[j];
+            *reinterpret_cast<uint4*>(sm.k + r * SM::QLD + vi * 8) = pk[j];
+            // K^T row d = 8 vi + e; token groups of four swizzled by d / 8 = vi
+            const bf16x8 x = __builtin_bit_cast(bf16x8, pk[j]);
+            const unsigned col = 4 * ((r >> 2) ^ vi) + (r & 3);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + col] = x[e];
+        }
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned hx = i / (kC * VPRV);
+            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
+            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
+        }
+        if (lead) {                          // gates of this head, lane = token
+            constexpr float kLog2e = 1.4426950408889634f;
+            const int ln = t & 63;
+            const float G2 = dev::wave_inclusive_sum(gpf * kLog2e, ln);
+            const float G2_last = __shfl(G2, kC - 1, 64);
+            float* gt = hd.gate[buf];
+            gt[GATE_G2 * kC + ln] = G2;
+            gt[GATE_GAM * kC + ln] = __builtin_amdgcn_exp2f(G2);
+            gt[GATE_BET * kC + ln] = bpf;
+            gt[GATE_KDEC * kC + ln] = __builtin_amdgcn_exp2f(G2_last - G2);
+        }
+    };
+    if (nchunks > 0) {
+        prefetch(0, (unsigned)tid);
+        stage(0, (unsigned)tid);
+    }
 
     for (int c = 0; c < nchunks; ++c) {
         int b0, e0;
@@ -270,88 +316,109 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         int tid_l = tid;
         asm volatile("" : "+v"(lane), "+v"(tid_l));
         const int li = lane & 15, g4 = lane >> 4;
-
-        // ---- stage this chunk's inputs.  No barrier is needed before: Q, K and V were
-        //      last read in phase 1 of the previous chunk, K^T and the gates go to the
-        //      other parity, and the blocks phase 1 writes are protected by the barrier
-        //      after staging.
         __bf16* kt = sm.kt[buf];
-#pragma unroll
-        for (int j = 0; j < NPF; ++j) {
-            const int i = tid_l + NT * j;
-            const int which = i / (kC * VPR);
-            const int r = (i / VPR) % kC, vi = i % VPR;
-            *reinterpret_cast<uint4*>((which == 0 ? sm.q : sm.k) + r * SM::QLD + vi * 8) = pf[j];
-            if (which == 1) {
-                const bf16x8 x = __builtin_bit_cast(bf16x8, pf[j]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + r] = x[e];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const int i = tid_l + NT * j;
-            const int hx = i / (kC * VPRV);
-            const int r = (i / VPRV) % kC, vi = i % VPRV;
-            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
-        }
-        if (lead) {                          // gates of this head, lane = token
-            constexpr float kLog2e = 1.4426950408889634f;
-            const float G2 = dev::wave_inclusive_sum(gpf * kLog2e, lane);
-            const float G2_last = __shfl(G2, kC - 1, 64);
-            float* gt = hd.gate[buf];
-            gt[GATE_G2 * kC + lane] = G2;
-            gt[GATE_GAM * kC + lane] = exp2f(G2);
-            gt[GATE_BET * kC + lane] = bpf;
-            gt[GATE_KDEC * kC + lane] = exp2f(G2_last - G2);
-        }
-        dev::lds_barrier();
-        // the staged inputs are in LDS: fetch the next chunk's behind this chunk's compute
-        if (c + 1 < nchunks) prefetch(c + 1, tid_l);
 
-        // ---- phase 1a: lower tiles of K K^T and Q K^T -> -A_ij, A_ii^T, P per head
-        for (int tt = wv; tt < 20; tt += NW) {
-            int i, j;
-            tile_ij(tt % 10, i, j);
-            const __bf16* X = tt < 10 ? sm.k : sm.q;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        dev::lds_barrier();
+        // chunk c's inputs are in LDS: fetch chunk c + 1's behind this chunk's compute
+        if (c + 1 < nchunks) prefetch(c + 1, (unsigned)tid_l);
+
+        // ---- phase 1.  The first wave of each head: its head's four diagonal K K^T
+        //      tiles -> A_bb (fp32, in LDS only it reads), then T_bb = (I + A_bb)^-1 by
+        //      forward substitution, lane 16 b + j computing column j of block b.  The
+        //      other waves: the sixteen shared tiles (off-diagonal K K^T -> -A_ij, and
+        //      Q K^T -> P) for every head.  Then every wave prepares its strip.
+        if (lead) {
+            const float* gt = hd.gate[buf];
 #pragma unroll
-            for (int kk = 0; kk < KS_DK; ++kk)
-                acc = mma32(ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4),
-                            ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4), acc);
-            // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
-            const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
+            for (int b = 0; b < 4; ++b) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < HG; ++x) {
-                typename SM::Head& hx = sm.hd[x];
-                const float* gt = hx.gate[buf];
+                for (int kk = 0; kk < KS_DK; ++kk)
+                    acc = mma32(ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4),
+                                ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4), acc);
+                const int r = 16 * b + li, s0 = 16 * b + 4 * g4;
                 const float G2r = gt[GATE_G2 * kC + r];
+                const float br = gt[GATE_BET * kC + r];
                 const f32x4 G2s = *reinterpret_cast<const f32x4*>(gt + GATE_G2 * kC + s0);
-                if (tt < 10) {
-                    const float br = gt[GATE_BET * kC + r];
-                    f32x4 val;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        val[e] = s0 + e < r ? br * acc[e] * exp2f(G2r - G2s[e]) : 0.f;
-                    if (i == j) {
+                for (int e = 0; e < 4; ++e)   // A[r][s] at row s, column r of the transposed block
+                    hd.at[b * SM::ATB + (4 * g4 + e) * SM::ATLD + li] =
+                        s0 + e < r ? br * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f;
+            }
+            const int b = g4, jc = li;
+            const float* AT = hd.at + b * SM::ATB;
+            float acc[16], t[16];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) hx.at[i * SM::ATB + (4 * g4 + e) * SM::ATLD + li] = val[e];
-                    } else {
-                        const Split4 sp = split4(-val);
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                t[s] = s < jc ? 0.f : (s == jc ? 1.f : acc[s]);
+                if (s < 15) {
+                    const float* row = AT + s * SM::ATLD;   // row s holds A[r][s] at column r
+#pragma unroll
+                    for (int r4 = (s + 1) / 4; r4 < 4; ++r4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4*>(row + 4 * r4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-av[e], t[s], acc[4 * r4 + e]);
+                    }
+                }
+            }
+            __bf16* th = hd.sol[blk(b, b)][0];
+            __bf16* tl = hd.sol[blk(b, b)][1];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const __bf16 x = (__bf16)t[r];
+                th[r * SM::BLD + jc] = x;
+                tl[r * SM::BLD + jc] = (__bf16)(t[r] - (float)x);
+            }
+        } else {
+            constexpr int NTI = (16 + NNL - 1) / NNL;
+            const int nl = wv - hh - 1;          // index among the waves that are not first
+#pragma unroll
+            for (int n = 0; n < NTI; ++n) {
+                const int tt = nl + NNL * n;     // wave-uniform: 0..5 K K^T, 6..15 Q K^T
+                if (tt >= 16) break;
+                int i, j;
+                if (tt < 6) {                    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                    i = 1 + (tt >= 1) + (tt >= 3);
+                    j = tt - (i - 1) * i / 2;
+                } else {
+                    tile_ij(tt - 6, i, j);
+                }
+                const __bf16* X = tt < 6 ? sm.k : sm.q;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk)
+                    acc = mma32(ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4),
+                                ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4), acc);
+                // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
+                const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
+#pragma unroll
+                for (int x = 0; x < HG; ++x) {
+                    typename SM::Head& hx = sm.hd[x];
+                    const float* gx = hx.gate[buf];
+                    const float G2r = gx[GATE_G2 * kC + r];
+                    const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
+                    f32x4 d;   // e^(G_r - G_s) where s <= r, else 1 (never used)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(s0 + e <= r ? G2r - G2s[e] : 0.f);
+                    if (tt < 6) {                // strictly below the diagonal
+                        const float br = gx[GATE_BET * kC + r];
+                        const Split4 sp = split4(-(br * acc * d));
                         st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
                         st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
-                    }
-                } else {
-                    bf16x4 pv4;
+                    } else {
+                        bf16x4 pv4;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pv4[e] = (__bf16)(s0 + e <= r ? acc[e] * exp2f(G2r - G2s[e]) : 0.f);
-                    st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
+                        for (int e = 0; e < 4; ++e) pv4[e] = (__bf16)(s0 + e <= r ? acc[e] * d[e] : 0.f);
+                        st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
+                    }
                 }
             }
         }
 
-        // ---- phase 1b: Z = K S and Q S for this strip; R = beta (V - gamma Z)
+        // this strip's Z = K S and Q S; R = beta (V - gamma Z); S scaled by gamma_last
         const float* gt = hd.gate[buf];
         f32x4 Racc[4][2], Oacc[4][2];
         {
@@ -393,40 +460,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[mt][nt] *= bet;
             }
         }
-        dev::lds_barrier();   // A, P and the gates of every head are complete
-
-        // ---- phase 2: T_bb = (I + A_bb)^-1 for the four diagonal blocks, first wave
-        //      of each head; lane 16 b + j computes column j of block b
-        if (lead) {
-            const int b = g4, jc = li;
-            const float* AT = hd.at + b * SM::ATB;
-            float acc[16], t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                t[s] = s < jc ? 0.f : (s == jc ? 1.f : acc[s]);
-                if (s < 15) {
-                    const float* row = AT + s * SM::ATLD;   // row s holds A[r][s] at column r
-#pragma unroll
-                    for (int r4 = (s + 1) / 4; r4 < 4; ++r4) {
-                        const f32x4 av = *reinterpret_cast<const f32x4*>(row + 4 * r4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-av[e], t[s], acc[4 * r4 + e]);
-                    }
-                }
-            }
-            __bf16* th = hd.sol[blk(b, b)][0];
-            __bf16* tl = hd.sol[blk(b, b)][1];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const __bf16 x = (__bf16)t[r];
-                th[r * SM::BLD + jc] = x;
-                tl[r * SM::BLD + jc] = (__bf16)(t[r] - (float)x);
-            }
-        }
-        dev::lds_barrier();   // T_ii blocks are complete
+        dev::lds_barrier();   // every -A_ij, T_ii and P block is complete
+        if (c + 1 < nchunks) stage(c + 1, (unsigned)tid_l);
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
@@ -497,7 +532,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
 #pragma unroll
             for (int mt = 0; mt < MT_S; ++mt) {
-                const bf16x8 ka = row_fromc(kt + (16 * mt + li) * SM::KTLD, kk, g4);
+                const int d = 16 * mt + li, sw = d >> 3;
+                const bf16x8 ka = cat8(ld4(kt + d * SM::KTLD + 4 * ((8 * kk + g4) ^ sw)),
+                                       ld4(kt + d * SM::KTLD + 4 * ((8 * kk + 4 + g4) ^ sw)));
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     Sacc[mt][nt] = mma32(ka, bh[nt], Sacc[mt][nt]);

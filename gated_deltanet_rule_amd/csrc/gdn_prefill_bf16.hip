@@ -140,7 +140,8 @@ struct Smem {
         __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
         __bf16 p[10][BSZ];                    // P blocks
-        float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
+        float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s];
+                                              // in phase 3 the output staging of the head's waves
         float gate[2][kGates * kC];           // by chunk parity
     } hd[HG];
 };
@@ -197,6 +198,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     Sacc[mt][nt][i] = src[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li];
+        // Wait for the state here, once: left pending, the wait would be placed at the
+        // state's first use inside the chunk loop and, executed every chunk, would also
+        // wait for that chunk's prefetch loads.  (s_waitcnt vmcnt(0), gfx9 encoding.)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
@@ -228,13 +233,13 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     auto ld16 = [](const void* base, uint32_t off) {
         return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
     };
-    auto prefetch = [&](int c, unsigned t) {
+    // chunk c's Q and K rows and (first wave of each head) its g and beta
+    auto prefetch_qk = [&](int c, unsigned t) {
         int b0, e0;
         dev::chunk_span(c, off64, len, b0, e0);
         const int tok = lo + b0, L = e0 - b0;
         const __bf16* qb = qg + ((size_t)tok * a.H_k + kh) * DK;
         const __bf16* kb = kg + ((size_t)tok * a.H_k + kh) * DK;
-        const __bf16* vb = vg + ((size_t)tok * a.H_v + h0) * DV;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const unsigned i = t + NT * j;
@@ -243,14 +248,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             const bool in = (int)r < L;
             pq[j] = in ? ld16(qb, off) : make_uint4(0u, 0u, 0u, 0u);
             pk[j] = in ? ld16(kb, off) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned hx = i / (kC * VPRV);
-            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
-            const uint32_t off = ((r * (unsigned)a.H_v + hx) * DV + vi * 8) * 2u;
-            pv[j] = (int)r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
         }
         if (lead) {
             const unsigned s = t & 63;
@@ -261,13 +258,27 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             bpf = (int)s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
         }
     };
-    // Write chunk c's prefetched inputs to LDS: Q, K and V rows, K^T and the gates
-    // (those two by chunk parity).  Runs before the loop for chunk 0 and, for chunk
-    // c + 1, right after the barrier that ends phase 2 of chunk c: Q, K and V were
-    // last read in phase 1, and the other parity of K^T and the gates was last read
-    // in phase 3 of chunk c - 1.  Doing it before phase 3 issues its stores also
-    // keeps the wait for the prefetch loads from waiting for those stores.
-    auto stage = [&](int c, unsigned t) {
+    // chunk c's V rows of the HG heads
+    auto prefetch_v = [&](int c, unsigned t) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const __bf16* vb = vg + ((size_t)tok * a.H_v + h0) * DV;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned hx = i / (kC * VPRV);
+            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
+            const uint32_t off = ((r * (unsigned)a.H_v + hx) * DV + vi * 8) * 2u;
+            pv[j] = (int)r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    // Write chunk c's prefetched Q and K rows, K^T and the gates (those two by chunk
+    // parity) to LDS.  For chunk c + 1 this runs right after the barrier that ends
+    // phase 1 of chunk c: Q and K were last read in phase 1, and the other parity of
+    // K^T and the gates was last read in phase 3 of chunk c - 1.  Doing it before
+    // phase 3 issues its stores keeps the wait for the loads from waiting for those.
+    auto stage_qk = [&](int c, unsigned t) {
         const int buf = c & 1;
         __bf16* kt = sm.kt[buf];
 #pragma unroll
@@ -282,13 +293,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + col] = x[e];
         }
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned hx = i / (kC * VPRV);
-            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
-            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
-        }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
             const int ln = t & 63;
@@ -301,9 +305,28 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             gt[GATE_KDEC * kC + ln] = __builtin_amdgcn_exp2f(G2_last - G2);
         }
     };
+    // Chunk c's V rows to LDS (for chunk c + 1 right after phase 1 of chunk c, the
+    // last reader of V).
+    auto stage_v = [&](unsigned t) {
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned hx = i / (kC * VPRV);
+            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
+            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
+        }
+    };
+    // Loads run a chunk ahead of their staging: right after phase 1 of chunk c,
+    // chunk c + 1's inputs are staged and chunk c + 2's are fetched.
     if (nchunks > 0) {
-        prefetch(0, (unsigned)tid);
-        stage(0, (unsigned)tid);
+        prefetch_qk(0, (unsigned)tid);
+        prefetch_v(0, (unsigned)tid);
+        stage_qk(0, (unsigned)tid);
+        stage_v((unsigned)tid);
+        if (nchunks > 1) {
+            prefetch_qk(1, (unsigned)tid);
+            prefetch_v(1, (unsigned)tid);
+        }
     }
 
     for (int c = 0; c < nchunks; ++c) {
@@ -319,8 +342,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         __bf16* kt = sm.kt[buf];
 
         dev::lds_barrier();
-        // chunk c's inputs are in LDS: fetch chunk c + 1's behind this chunk's compute
-        if (c + 1 < nchunks) prefetch(c + 1, (unsigned)tid_l);
 
         // ---- phase 1.  The first wave of each head: its head's four diagonal K K^T
         //      tiles -> A_bb (fp32, in LDS only it reads), then T_bb = (I + A_bb)^-1 by
@@ -364,8 +385,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                     }
                 }
             }
-            __bf16* th = hd.sol[blk(b, b)][0];
-            __bf16* tl = hd.sol[blk(b, b)][1];
+            const int bb = (0x9520 >> (4 * b)) & 15;   // blk(b, b) for b = 0..3
+            __bf16* th = hd.sol[bb][0];
+            __bf16* tl = hd.sol[bb][1];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const __bf16 x = (__bf16)t[r];
@@ -461,11 +483,21 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
         }
         dev::lds_barrier();   // every -A_ij, T_ii and P block is complete
-        if (c + 1 < nchunks) stage(c + 1, (unsigned)tid_l);
+        if (c + 1 < nchunks) {
+            stage_qk(c + 1, (unsigned)tid_l);
+            stage_v((unsigned)tid_l);
+        }
+        if (c + 2 < nchunks) {
+            prefetch_qk(c + 2, (unsigned)tid_l);
+            prefetch_v(c + 2, (unsigned)tid_l);
+        }
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
+        constexpr int OLD = 40;                                        // O staging rows (bf16)
+        static_assert(NWH * 16 * OLD * 2 <= 4 * SM::ATB * 4, "output staging must fit the A_ii space");
+        __bf16* oslot = reinterpret_cast<__bf16*>(hd.at) + (wv - hh * NWH) * 16 * OLD;
         Split4 Us[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -505,16 +537,20 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                     Oacc[i][nt] = mma32(pa, cat8(Us[j0][nt].lo, l1), Oacc[i][nt]);
                 }
             }
+            // out through LDS (this wave's slot in its head's A_ii space, unused in phase 3):
+            // one 16-byte store per lane per row block
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * i + 4 * g4 + e;
-                    const uint32_t off = (uint32_t)(r * a.H_v * DV + 16 * nt + li) * 2u;
-                    if (r < L)
-                        *reinterpret_cast<__bf16*>(reinterpret_cast<char*>(obase) + off) =
-                            (__bf16)(a.scale * Oacc[i][nt][e]);
-                }
+                for (int e = 0; e < 4; ++e)
+                    oslot[(4 * g4 + e) * OLD + 16 * nt + li] = (__bf16)(a.scale * Oacc[i][nt][e]);
+            {
+                const int row = lane >> 2, q = lane & 3;
+                const uint4 x = *reinterpret_cast<const uint4*>(oslot + row * OLD + 8 * q);
+                const int r = 16 * i + row;
+                const uint32_t off = (uint32_t)(r * a.H_v * DV + 8 * q) * 2u;
+                if (r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(obase) + off) = x;
+            }
         }
 
         // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs

@@ -78,15 +78,20 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 struct Split4 { bf16x4 hi, lo; };
 
-// x = hi + lo: hi rounded to bf16, lo the exact remainder rounded once
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo: hi rounded to bf16, lo the exact remainder rounded once (two values
+// per conversion instruction)
 __device__ __forceinline__ Split4 split4(f32x4 x) {
+    const f32x2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
+    const bf16x2 h01 = __builtin_convertvector(x01, bf16x2);
+    const bf16x2 h23 = __builtin_convertvector(x23, bf16x2);
+    const bf16x2 l01 = __builtin_convertvector(x01 - __builtin_convertvector(h01, f32x2), bf16x2);
+    const bf16x2 l23 = __builtin_convertvector(x23 - __builtin_convertvector(h23, f32x2), bf16x2);
     Split4 s;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        s.hi[e] = h;
-        s.lo[e] = (__bf16)(x[e] - (float)h);
-    }
+    s.hi = bf16x4{h01[0], h01[1], h23[0], h23[1]};
+    s.lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
     return s;
 }
 
@@ -108,12 +113,13 @@ __device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g) {
 
 // B operand (from-C order, k step ks) out of a pair of state accumulator tiles
 __device__ __forceinline__ bf16x8 state_frag(const f32x4& t0, const f32x4& t1) {
+    const bf16x2 a = __builtin_convertvector(f32x2{t0[0], t0[1]}, bf16x2);
+    const bf16x2 b = __builtin_convertvector(f32x2{t0[2], t0[3]}, bf16x2);
+    const bf16x2 c = __builtin_convertvector(f32x2{t1[0], t1[1]}, bf16x2);
+    const bf16x2 d = __builtin_convertvector(f32x2{t1[2], t1[3]}, bf16x2);
     bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = (__bf16)t0[i];
-        r[4 + i] = (__bf16)t1[i];
-    }
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
     return r;
 }
 
@@ -135,7 +141,7 @@ struct Smem {
     __bf16 k[kC * QLD];
     __bf16 kt[2][DK * KTLD];                  // K^T, by chunk parity (the state update of
                                               // chunk c reads it while chunk c+1 is staged);
-                                              // row d holds token group q at group q ^ (d / 8)
+                                              // row d holds token group q at group q ^ (d / 16)
     struct Head {
         __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
@@ -214,6 +220,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     const int64_t pos0 = a.start_pos ? a.start_pos[seq] : 0;
     const int off64 = (int)(pos0 & (kC - 1));
     const int nchunks = dev::seq_chunks(len, off64);
+    // next grid point after pos0 and the number of grid states exported so far
+    int64_t next_export = a.export_grid > 0 ? (pos0 / a.export_grid + 1) * a.export_grid : 0;
+    int64_t exported = 0;
 
     const __bf16* qg = static_cast<const __bf16*>(a.q);
     const __bf16* kg = static_cast<const __bf16*>(a.k);
@@ -287,9 +296,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             const unsigned r = i / VPR, vi = i % VPR;
             *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + vi * 8) = pq[j];
             *reinterpret_cast<uint4*>(sm.k + r * SM::QLD + vi * 8) = pk[j];
-            // K^T row d = 8 vi + e; token groups of four swizzled by d / 8 = vi
+            // K^T row d = 8 vi + e; token groups of four swizzled by d / 16 = vi / 2
             const bf16x8 x = __builtin_bit_cast(bf16x8, pk[j]);
-            const unsigned col = 4 * ((r >> 2) ^ vi) + (r & 3);
+            const unsigned col = 4 * ((r >> 2) ^ (vi >> 1)) + (r & 3);
 #pragma unroll
             for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + col] = x[e];
         }
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                     } else {
                         bf16x4 pv4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pv4[e] = (__bf16)(s0 + e <= r ? acc[e] * d[e] : 0.f);
+                        for (int e = 0; e < 4; ++e) pv4[e] = (__bf16)(s0 + e <= r ? a.scale * acc[e] * d[e] : 0.f);
                         st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
                     }
                 }
@@ -475,7 +484,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             const f32x4 bet = *reinterpret_cast<const f32x4*>(gt + GATE_BET * kC + 16 * mt + 4 * g4);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                Oacc[mt][nt] *= gam;
+                Oacc[mt][nt] *= a.scale * gam;
                 // + V through V I, onto -gamma Z
                 const bf16x4 av = ld4(hd.v + (16 * mt + li) * SM::VLD + col0 + 16 * nt + 4 * g4);
                 Racc[mt][nt] = mma16(av, ident, -gam * Racc[mt][nt]);
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    oslot[(4 * g4 + e) * OLD + 16 * nt + li] = (__bf16)(a.scale * Oacc[i][nt][e]);
+                    oslot[(4 * g4 + e) * OLD + 16 * nt + li] = (__bf16)Oacc[i][nt][e];
             {
                 const int row = lane >> 2, q = lane & 3;
                 const uint4 x = *reinterpret_cast<const uint4*>(oslot + row * OLD + 8 * q);
@@ -554,6 +563,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         }
 
         // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs
+        const __bf16* krow[4];                // this lane's K^T row li, swizzle part g4 ^ m
+#pragma unroll
+        for (int m = 0; m < 4; ++m) krow[m] = kt + li * SM::KTLD + 4 * (g4 ^ m);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const f32x4 kd0 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 4 * g4);
@@ -568,9 +580,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
 #pragma unroll
             for (int mt = 0; mt < MT_S; ++mt) {
-                const int d = 16 * mt + li, sw = d >> 3;
-                const bf16x8 ka = cat8(ld4(kt + d * SM::KTLD + 4 * ((8 * kk + g4) ^ sw)),
-                                       ld4(kt + d * SM::KTLD + 4 * ((8 * kk + 4 + g4) ^ sw)));
+                // row d = 16 mt + li, groups (8 kk + 4 h + g4) ^ mt = (8 kk + 4 (h ^ mt / 4)) + (g4 ^ mt % 4)
+                const __bf16* kr = krow[mt & 3] + 16 * mt * SM::KTLD;
+                const bf16x8 ka = cat8(ld4(kr + 4 * (8 * kk + 4 * (0 ^ (mt >> 2)))),
+                                       ld4(kr + 4 * (8 * kk + 4 * (1 ^ (mt >> 2)))));
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     Sacc[mt][nt] = mma32(ka, bh[nt], Sacc[mt][nt]);
@@ -582,9 +595,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         // ---- export on the grid
         if (a.export_grid > 0) {
             const int64_t p_end = pos0 + e0;
-            if (p_end % a.export_grid == 0) {
-                const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
-                const int64_t idx = (int64_t)a.export_offsets[seq] + m;
+            if (p_end == next_export) {
+                const int64_t idx = (int64_t)a.export_offsets[seq] + exported;
+                next_export += a.export_grid;
+                ++exported;
                 if (idx >= 0 && idx < a.export_capacity) {
                     float* dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
 #pragma unroll

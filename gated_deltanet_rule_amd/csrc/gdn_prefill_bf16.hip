@@ -361,11 +361,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             const float* gt = hd.gate[buf];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
+                bf16x8 kf[KS_DK];             // both operands are this block's K rows
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk)
-                    acc = mma32(ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4),
-                                ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4), acc);
+                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(kf[kk], kf[kk], acc);
                 const int r = 16 * b + li, s0 = 16 * b + 4 * g4;
                 const float G2r = gt[GATE_G2 * kC + r];
                 const float br = gt[GATE_BET * kC + r];
@@ -380,19 +381,28 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             float acc[16], t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            // row s of the transposed block holds A[r][s] at column r; rows are read two
+            // steps before they are used, so the LDS latency overlaps the arithmetic
+            f32x4 rows[3][4];
+            auto load_row = [&](int s) {
+#pragma unroll
+                for (int r4 = (s + 1) / 4; r4 < 4; ++r4)
+                    rows[s % 3][r4] = *reinterpret_cast<const f32x4*>(AT + s * SM::ATLD + 4 * r4);
+            };
+            load_row(0);
+            load_row(1);
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
+                if (s + 2 < 15) load_row(s + 2);
                 t[s] = s < jc ? 0.f : (s == jc ? 1.f : acc[s]);
                 if (s < 15) {
-                    const float* row = AT + s * SM::ATLD;   // row s holds A[r][s] at column r
 #pragma unroll
-                    for (int r4 = (s + 1) / 4; r4 < 4; ++r4) {
-                        const f32x4 av = *reinterpret_cast<const f32x4*>(row + 4 * r4);
+                    for (int r4 = (s + 1) / 4; r4 < 4; ++r4)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-av[e], t[s], acc[4 * r4 + e]);
-                    }
+                            if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-rows[s % 3][r4][e], t[s], acc[4 * r4 + e]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             const int bb = (0x9520 >> (4 * b)) & 15;   // blk(b, b) for b = 0..3
             __bf16* th = hd.sol[bb][0];
@@ -418,11 +428,15 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                     tile_ij(tt - 6, i, j);
                 }
                 const __bf16* X = tt < 6 ? sm.k : sm.q;
+                bf16x8 fa[KS_DK], fb[KS_DK];
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    fa[kk] = ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4);
+                    fb[kk] = ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4);
+                }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk)
-                    acc = mma32(ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4),
-                                ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4), acc);
+                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(fa[kk], fb[kk], acc);
                 // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
                 const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
 #pragma unroll
@@ -562,35 +576,54 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
         }
 
-        // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs
+        // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs.  The B operands
+        // first; then the K^T reads run two steps ahead of the MFMAs that use them.
         const __bf16* krow[4];                // this lane's K^T row li, swizzle part g4 ^ m
 #pragma unroll
         for (int m = 0; m < 4; ++m) krow[m] = kt + li * SM::KTLD + 4 * (g4 ^ m);
+        bf16x8 bh[2][2], bl[2][2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const f32x4 kd0 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 4 * g4);
             const f32x4 kd1 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 16 + 4 * g4);
-            bf16x8 bh[2], bl[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const Split4 s0 = split4(Racc[2 * kk][nt] * kd0);
                 const Split4 s1 = split4(Racc[2 * kk + 1][nt] * kd1);
-                bh[nt] = cat8(s0.hi, s1.hi);
-                bl[nt] = cat8(s0.lo, s1.lo);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-                // row d = 16 mt + li, groups (8 kk + 4 h + g4) ^ mt = (8 kk + 4 (h ^ mt / 4)) + (g4 ^ mt % 4)
-                const __bf16* kr = krow[mt & 3] + 16 * mt * SM::KTLD;
-                const bf16x8 ka = cat8(ld4(kr + 4 * (8 * kk + 4 * (0 ^ (mt >> 2)))),
-                                       ld4(kr + 4 * (8 * kk + 4 * (1 ^ (mt >> 2)))));
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    Sacc[mt][nt] = mma32(ka, bh[nt], Sacc[mt][nt]);
-                    Sacc[mt][nt] = mma32(ka, bl[nt], Sacc[mt][nt]);
-                }
+                bh[kk][nt] = cat8(s0.hi, s1.hi);
+                bl[kk][nt] = cat8(s0.lo, s1.lo);
             }
         }
+        // step t = (mt, kk) = (t / 2, t % 2); row d = 16 mt + li, token groups
+        // (8 kk + 4 h + g4) ^ mt = (8 kk + 4 (h ^ mt / 4)) + (g4 ^ mt % 4)
+        auto kfrag = [&](int t) {
+            const int mt = t >> 1, kk = t & 1;
+            const __bf16* kr = krow[mt & 3] + 16 * mt * SM::KTLD;
+            return cat8(ld4(kr + 4 * (8 * kk + 4 * (0 ^ (mt >> 2)))), ld4(kr + 4 * (8 * kk + 4 * (1 ^ (mt >> 2)))));
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            constexpr int NSTEP = 2 * MT_S;
+            bf16x8 ka[3];
+            ka[0] = kfrag(0);
+            ka[1] = kfrag(1);
+#pragma unroll
+            for (int t = 0; t < NSTEP; ++t) {
+                if (t + 2 < NSTEP) ka[(t + 2) % 3] = kfrag(t + 2);
+                const int mt = t >> 1, kk = t & 1;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    Sacc[mt][nt] = mma32(ka[t % 3], bh[kk][nt], Sacc[mt][nt]);
+                    Sacc[mt][nt] = mma32(ka[t % 3], bl[kk][nt], Sacc[mt][nt]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NSTEP; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // four MFMAs
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- export on the grid
         if (a.export_grid > 0) {

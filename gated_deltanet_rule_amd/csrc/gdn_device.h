@@ -29,13 +29,21 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int i, int64_t T, i
     len = (int)(e - b);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele, fixed order).
-__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+// Inclusive prefix sum over the 64 lanes of a wave, in a fixed order: shifted adds
+// within each row of 16 lanes (DPP row_shr 1, 2, 4, 8), then the last lane of row 0
+// and of row 2 added to rows 1 and 3 (row_bcast:15), then lane 31 added to rows 2
+// and 3 (row_bcast:31).  Lanes that a shift or broadcast does not reach add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_term(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_term<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_term<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_term<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_term<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_term<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_term<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 

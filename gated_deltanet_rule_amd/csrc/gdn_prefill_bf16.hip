@@ -305,8 +305,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
             const int ln = t & 63;
-            const float G2 = dev::wave_inclusive_sum(gpf * kLog2e, ln);
-            const float G2_last = __shfl(G2, kC - 1, 64);
+            const float G2 = dev::wave_inclusive_sum(gpf * kLog2e);
+            const float G2_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G2), kC - 1));
             float* gt = hd.gate[buf];
             gt[GATE_G2 * kC + ln] = G2;
             gt[GATE_GAM * kC + ln] = __builtin_amdgcn_exp2f(G2);

@@ -32,7 +32,7 @@ METRIC = "GDN prefill tokens/s + decode state GB/s (frac of HBM peak) on 1 MI355
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 CHUNK = 64
-KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "scan_kernel": "gdn_prefill.hip"}
+KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "chunk_kernel": "gdn_prefill_bf16.hip"}
 
 
 def parse():
@@ -205,13 +205,13 @@ def main():
                           "bytes_per_launch": dec_bytes, "traffic": measured_traffic("decode_kernel")},
         # arithmetic intensity pre_flops / pre_bytes (about 156 flop/B) is below the bf16
         # ridge (2500 / 8 = 312 flop/B): HBM binds, MFMA use is reported beside it
-        "scan_kernel": {"ms": round(t_pre, 4), "bound": "hbm", "achieved": round(pre_gbps, 1),
+        "chunk_kernel": {"ms": round(t_pre, 4), "bound": "hbm", "achieved": round(pre_gbps, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
-                        "bytes_per_launch": pre_bytes, "traffic": measured_traffic("scan_kernel"),
+                        "bytes_per_launch": pre_bytes, "traffic": measured_traffic("chunk_kernel"),
                         "mfma_tflops": round(pre_tflops, 2), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                         "flops_per_launch": pre_flops},
     }
-    dominant = "scan_kernel" if t_pre >= t_dec else "decode_kernel"
+    dominant = "chunk_kernel" if t_pre >= t_dec else "decode_kernel"
     roof = kernels[dominant]
     roofline = {"kernel": dominant, "bound": roof["bound"], "achieved": roof["achieved"], "peak": roof["peak"],
                 "unit": roof["unit"], "frac": roof["frac"], "traffic": roof["traffic"]}

@@ -177,8 +177,13 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 
     const int G = a.H_v / a.H_k;
     const int GG = G / HG;
-    const int seq = blockIdx.x / (a.H_k * GG);
-    const int rem = blockIdx.x - seq * (a.H_k * GG);
+    // Workgroups go to the 8 XCDs round robin by index.  Renumber them so that each
+    // XCD receives a contiguous run of (sequence, key head) units: the workgroups of
+    // one sequence then share one L2, which holds the g and beta lines they all read.
+    unsigned wg = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
+    const int seq = (int)wg / (a.H_k * GG);
+    const int rem = (int)wg - seq * (a.H_k * GG);
     const int kh = rem / GG;
     const int h0 = kh * G + (rem - kh * GG) * HG;
     const int tid = threadIdx.x;

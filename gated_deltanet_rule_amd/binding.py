@@ -45,11 +45,11 @@ SIGNATURES = {
     "gdn_recurrent_decode": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _i32, _vp, _vp, _vp]),
     "gdn_chunk_prefill": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
-                                         _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _sz,
-                                         _vp]),
+                                         _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp,
+                                         _sz, _vp]),
     "gdn_mixed_step": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp,
-                                      _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64,
-                                      _vp, _sz, _vp]),
+                                      _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                      _i64, _vp, _sz, _vp]),
     "gdn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -181,7 +181,7 @@ def gdn_recurrent_decode(q, k, v, g, beta, o, state_pool, slot_in, slot_out, *, 
 
 
 def _prefill_common(dev, num_seqs, cu_seqlens, init_slot, final_slot, start_pos, export_grid,
-                    export_states, export_offsets_t, workspace, H_v, d_k, d_v):
+                    export_states, export_offsets_t, export_slots, workspace, H_v, d_k, d_v):
     _index(cu_seqlens, "cu_seqlens", num_seqs + 1, dev)
     _index(init_slot, "init_slot", num_seqs, dev)
     _index(final_slot, "final_slot", num_seqs, dev)
@@ -189,7 +189,10 @@ def _prefill_common(dev, num_seqs, cu_seqlens, init_slot, final_slot, start_pos,
     n_exp = 0
     if export_grid:
         _index(export_offsets_t, "export_offsets", num_seqs + 1, dev)
-        if export_states is not None:
+        if export_slots is not None:
+            _need(export_slots, "export_slots", dtype=torch.int32, device=dev, ndim=1)
+            n_exp = export_slots.shape[0]
+        elif export_states is not None:
             _need(export_states, "export_states", dtype=torch.float32, device=dev, ndim=4)
             if tuple(export_states.shape[1:]) != (H_v, d_k, d_v):
                 raise ValueError("export_states must be [E, %d, %d, %d]" % (H_v, d_k, d_v))
@@ -201,33 +204,35 @@ def _prefill_common(dev, num_seqs, cu_seqlens, init_slot, final_slot, start_pos,
 
 
 def _prefill_call(entry, q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot, scale, workspace,
-                  start_pos, export_grid, export_states, export_offsets, stream):
+                  start_pos, export_grid, export_states, export_offsets, export_slots, stream):
     T = q.shape[0]
     dev, H_k, H_v, d_k, d_v = _heads(q, k, v, g, beta, o, T)
     num_slots = _pool(state_pool, dev, H_v, d_k, d_v)
     N = cu_seqlens.shape[0] - 1
     n_exp, ws_bytes = _prefill_common(dev, N, cu_seqlens, init_slot, final_slot, start_pos, export_grid,
-                                      export_states, export_offsets, workspace, H_v, d_k, d_v)
+                                      export_states, export_offsets, export_slots, workspace, H_v, d_k, d_v)
     shape = make_shape(H_k, H_v, d_k, d_v, _dtype_code(q), scale)
     with torch.cuda.device(dev):
         _check(getattr(library(), entry)(
             ctypes.byref(shape), N, T, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(o), _ptr(state_pool), num_slots, _ptr(init_slot), _ptr(final_slot), _ptr(start_pos),
-            int(export_grid), _ptr(export_states), _ptr(export_offsets), n_exp, _ptr(workspace), ws_bytes,
-            _stream(dev, stream)))
+            int(export_grid), _ptr(export_states), _ptr(export_offsets), _ptr(export_slots), n_exp,
+            _ptr(workspace), ws_bytes, _stream(dev, stream)))
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot, *,
                       scale: float, workspace=None, start_pos=None, export_grid: int = 0,
-                      export_states=None, export_offsets=None, stream=None) -> None:
-    """Chunked prefill over len(cu_seqlens) - 1 packed sequences (see include/gdn.h)."""
+                      export_states=None, export_offsets=None, export_slots=None, stream=None) -> None:
+    """Chunked prefill over len(cu_seqlens) - 1 packed sequences (see include/gdn.h).
+    Exports go to export_states, or straight into state_pool slots when export_slots
+    (one int32 slot per export) is given."""
     _prefill_call("gdn_chunk_prefill", q, k, v, g, beta, o, cu_seqlens, state_pool, init_slot, final_slot,
-                  scale, workspace, start_pos, export_grid, export_states, export_offsets, stream)
+                  scale, workspace, start_pos, export_grid, export_states, export_offsets, export_slots, stream)
 
 
 def gdn_mixed_step(q, k, v, g, beta, o, state_pool, slot_in, slot_out, cu_seqlens_prefill, init_slot,
                    final_slot, *, scale: float, workspace=None, start_pos=None, export_grid: int = 0,
-                   export_states=None, export_offsets=None, stream=None) -> None:
+                   export_states=None, export_offsets=None, export_slots=None, stream=None) -> None:
     """One mixed step: rows [0, len(slot_in)) decode, the rest prefill (see include/gdn.h)."""
     T = q.shape[0]
     dev, H_k, H_v, d_k, d_v = _heads(q, k, v, g, beta, o, T)
@@ -237,14 +242,15 @@ def gdn_mixed_step(q, k, v, g, beta, o, state_pool, slot_in, slot_out, cu_seqlen
     _index(slot_out, "slot_out", B, dev)
     N = cu_seqlens_prefill.shape[0] - 1
     n_exp, ws_bytes = _prefill_common(dev, N, cu_seqlens_prefill, init_slot, final_slot, start_pos,
-                                      export_grid, export_states, export_offsets, workspace, H_v, d_k, d_v)
+                                      export_grid, export_states, export_offsets, export_slots, workspace,
+                                      H_v, d_k, d_v)
     shape = make_shape(H_k, H_v, d_k, d_v, _dtype_code(q), scale)
     with torch.cuda.device(dev):
         _check(library().gdn_mixed_step(
             ctypes.byref(shape), B, _ptr(slot_in), _ptr(slot_out), N, T - B, _ptr(cu_seqlens_prefill),
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(state_pool), num_slots,
             _ptr(init_slot), _ptr(final_slot), _ptr(start_pos), int(export_grid), _ptr(export_states),
-            _ptr(export_offsets), n_exp, _ptr(workspace), ws_bytes, _stream(dev, stream)))
+            _ptr(export_offsets), _ptr(export_slots), n_exp, _ptr(workspace), ws_bytes, _stream(dev, stream)))
 
 
 def alloc_workspace(H_v: int, dtype: torch.dtype, num_seqs: int, total_tokens: int, device) -> torch.Tensor:

@@ -91,8 +91,8 @@ gdn_status check_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total
                          const float* g, const float* beta, void* o, float* state_pool,
                          int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
                          const int32_t* start_pos, int32_t export_grid, float* export_states,
-                         const int32_t* export_offsets, int64_t num_export_states, void* workspace,
-                         size_t workspace_bytes) {
+                         const int32_t* export_offsets, const int32_t* export_slots,
+                         int64_t num_export_states, void* workspace, size_t workspace_bytes) {
     gdn_status st = check_shape(shape);
     if (st != GDN_OK) return st;
     if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
@@ -131,7 +131,8 @@ gdn_status check_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total
         st = check_ptrs({{"export_offsets", export_offsets, 4}});
         if (st != GDN_OK) return st;
         if (num_export_states > 0) {
-            st = check_ptrs({{"export_states", export_states, 16}});
+            st = export_slots ? check_ptrs({{"export_slots", export_slots, 4}})
+                              : check_ptrs({{"export_states", export_states, 16}});
             if (st != GDN_OK) return st;
         }
     }
@@ -175,8 +176,8 @@ gdn::PrefillArgs prefill_args(const gdn_shape* s, int32_t num_seqs, int64_t tota
                               const float* g, const float* beta, void* o, float* pool, int32_t num_slots,
                               const int32_t* init_slot, const int32_t* final_slot,
                               const int32_t* start_pos, int32_t export_grid, float* export_states,
-                              const int32_t* export_offsets, int64_t num_export_states,
-                              void* workspace) {
+                              const int32_t* export_offsets, const int32_t* export_slots,
+                              int64_t num_export_states, void* workspace) {
     gdn::PrefillArgs a;
     a.H_k = s->num_k_heads;
     a.H_v = s->num_v_heads;
@@ -199,9 +200,10 @@ gdn::PrefillArgs prefill_args(const gdn_shape* s, int32_t num_seqs, int64_t tota
     a.final_slot = final_slot;
     a.start_pos = start_pos;
     a.export_grid = export_grid;
-    a.export_states = export_grid > 0 ? export_states : nullptr;
+    a.export_slots = export_grid > 0 ? export_slots : nullptr;
+    a.export_states = export_grid > 0 && !export_slots ? export_states : nullptr;
     a.export_offsets = export_grid > 0 ? export_offsets : nullptr;
-    a.export_capacity = export_grid > 0 && export_states ? num_export_states : 0;
+    a.export_capacity = export_grid > 0 && (a.export_states || a.export_slots) ? num_export_states : 0;
     a.workspace = workspace;
     return a;
 }
@@ -234,18 +236,20 @@ gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t t
                              const float* g, const float* beta, void* o, float* state_pool,
                              int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
                              const int32_t* start_pos, int32_t export_grid, float* export_states,
-                             const int32_t* export_offsets, int64_t num_export_states, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             const int32_t* export_offsets, const int32_t* export_slots,
+                             int64_t num_export_states, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
     g_last_error.clear();
     gdn_status st = check_prefill(shape, num_seqs, total_tokens, cu_seqlens, q, k, v, g, beta, o,
                                   state_pool, num_slots, init_slot, final_slot, start_pos, export_grid,
-                                  export_states, export_offsets, num_export_states, workspace,
-                                  workspace_bytes);
+                                  export_states, export_offsets, export_slots, num_export_states,
+                                  workspace, workspace_bytes);
     if (st != GDN_OK || num_seqs == 0) return st;
     return hip_status(gdn::launch_prefill(prefill_args(shape, num_seqs, total_tokens, cu_seqlens, q, k, v,
                                                        g, beta, o, state_pool, num_slots, init_slot,
                                                        final_slot, start_pos, export_grid, export_states,
-                                                       export_offsets, num_export_states, workspace),
+                                                       export_offsets, export_slots, num_export_states,
+                                                       workspace),
                                           stream),
                       "prefill launch");
 }
@@ -256,8 +260,8 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const
                           const float* g, const float* beta, void* o, float* state_pool, int32_t num_slots,
                           const int32_t* init_slot, const int32_t* final_slot, const int32_t* start_pos,
                           int32_t export_grid, float* export_states, const int32_t* export_offsets,
-                          int64_t num_export_states, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          const int32_t* export_slots, int64_t num_export_states, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
     g_last_error.clear();
     gdn_status st = check_decode(shape, num_decode_rows, q, k, v, g, beta, o, state_pool, num_slots,
                                  slot_in, slot_out);
@@ -273,7 +277,7 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const
     const float* bp = beta + B * shape->num_v_heads;
     st = check_prefill(shape, num_prefill_seqs, prefill_tokens, cu_seqlens_prefill, qp, kp, vp, gp, bp, op,
                        state_pool, num_slots, init_slot, final_slot, start_pos, export_grid, export_states,
-                       export_offsets, num_export_states, workspace, workspace_bytes);
+                       export_offsets, export_slots, num_export_states, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     // cached rows first, through the same launcher and kernel as a decode-only step
     if (num_decode_rows > 0) {
@@ -288,7 +292,7 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const
                                                        cu_seqlens_prefill, qp, kp, vp, gp, bp, op, state_pool,
                                                        num_slots, init_slot, final_slot, start_pos,
                                                        export_grid, export_states, export_offsets,
-                                                       num_export_states, workspace),
+                                                       export_slots, num_export_states, workspace),
                                           stream),
                       "mixed-step prefill launch");
 }

@@ -48,6 +48,7 @@ struct PrefillArgs {
     int export_grid;
     float* export_states;
     const int32_t* export_offsets;
+    const int32_t* export_slots;     // when set, exports go to pool[export_slots[idx]]
     int64_t export_capacity;
     void* workspace;
 };

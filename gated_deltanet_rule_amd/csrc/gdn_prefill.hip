@@ -734,8 +734,16 @@ __global__ __launch_bounds__(HG * DV * 2) void scan_kernel(PrefillArgs a) {
             if (p_end % a.export_grid == 0) {
                 const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
                 const int64_t idx = (int64_t)a.export_offsets[seq] + m;
+                float* dst = nullptr;
                 if (idx >= 0 && idx < a.export_capacity) {
-                    float* dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                    if (!a.export_slots) {
+                        dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                    } else {                    // straight into a cache slot
+                        const int sl = a.export_slots[idx];
+                        if (sl >= 0 && sl < a.num_slots) dst = a.pool + ((size_t)sl * a.H_v + h) * SE;
+                    }
+                }
+                if (dst) {
 #pragma unroll
                     for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll

@@ -637,8 +637,16 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 const int64_t idx = (int64_t)a.export_offsets[seq] + exported;
                 next_export += a.export_grid;
                 ++exported;
+                float* dst = nullptr;
                 if (idx >= 0 && idx < a.export_capacity) {
-                    float* dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                    if (!a.export_slots) {
+                        dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                    } else {                    // straight into a cache slot
+                        const int sl = a.export_slots[idx];
+                        if (sl >= 0 && sl < a.num_slots) dst = a.pool + ((size_t)sl * a.H_v + h) * SE;
+                    }
+                }
+                if (dst) {
 #pragma unroll
                     for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll

@@ -146,11 +146,21 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows,
  *              p % export_grid == 0 and start_pos < p <= start_pos + length is written
  *              to export_states[export_offsets[i] + m] (m counts sequence i's grid
  *              points in ascending order).
- *   export_states  device [sum of export counts, num_v_heads, d_k, d_v] fp32, written.
+ *   export_states  device [sum of export counts, num_v_heads, d_k, d_v] fp32, written;
+ *              unused (may be NULL) when export_slots is given.
  *   export_offsets device [num_seqs + 1] int32, the exclusive prefix sum of the
  *              per-sequence export counts (floor((s+L)/grid) - floor(s/grid)).
- *   num_export_states  how many states export_states holds; an export whose index
- *              would reach it is dropped (the kernels never write past the buffer).
+ *   export_slots   device [num_export_states] int32 or NULL.  When given, export idx
+ *              is written straight into the cache: state_pool[export_slots[idx]]
+ *              (skipped when the slot is outside [0, num_slots)), so a caller's block
+ *              table can route each grid state into its prefix-cache block ("[V1][Hybrid]
+ *              GatedDeltaNet Automatic Prefix Caching", section "Purpose": the returned
+ *              chunk history is replayed into persistent cache blocks).  Export slots
+ *              must differ from every slot the call reads (init_slot; in a mixed step
+ *              also slot_in) and from each other.
+ *   num_export_states  how many exports export_states (or export_slots) holds; an
+ *              export whose index would reach it is dropped (the kernels never write
+ *              past the buffer).
  *   workspace  device scratch of at least gdn_chunk_prefill_workspace_size() bytes,
  *              256-byte aligned, contents need no initialisation; may be NULL when
  *              that size is 0.
@@ -163,8 +173,9 @@ gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t t
                              float* state_pool, int32_t num_slots, const int32_t* init_slot,
                              const int32_t* final_slot, const int32_t* start_pos,
                              int32_t export_grid, float* export_states,
-                             const int32_t* export_offsets, int64_t num_export_states,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+                             const int32_t* export_offsets, const int32_t* export_slots,
+                             int64_t num_export_states, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * One mixed decode-plus-prefill step: tokens [0, num_decode_rows) are cached decode
@@ -187,8 +198,9 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows,
                           float* state_pool, int32_t num_slots, const int32_t* init_slot,
                           const int32_t* final_slot, const int32_t* start_pos,
                           int32_t export_grid, float* export_states,
-                          const int32_t* export_offsets, int64_t num_export_states,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          const int32_t* export_offsets, const int32_t* export_slots,
+                          int64_t num_export_states, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* Message describing the last non-OK status returned on the calling thread ("" if
  * none).  The pointer stays valid until the thread's next call into the library. */

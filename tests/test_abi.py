@@ -57,14 +57,14 @@ def _decode(shape=None, num_rows=4, q=FAKE, num_slots=8, slot_out=None):
 
 
 def _prefill(shape=None, num_seqs=2, total_tokens=100, export_grid=0, q=FAKE, cu=FAKE, ws_bytes=0,
-             num_export=0, init_slot=None, export_offsets=FAKE):
+             num_export=0, init_slot=None, export_offsets=FAKE, export_slots=None):
     # guard: init_slot is NULL unless a test passes one, and validation rejects that
     # after every check the tests below exercise
     lib = B.library()
     shape = shape or B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
     st = lib.gdn_chunk_prefill(ctypes.byref(shape), num_seqs, total_tokens, cu, q, FAKE, FAKE, FAKE, FAKE,
                                FAKE, FAKE, 8, init_slot, FAKE, None, export_grid, FAKE, export_offsets,
-                               num_export, FAKE, ws_bytes, None)
+                               export_slots, num_export, FAKE, ws_bytes, None)
     return st, B.gdn_last_error()
 
 
@@ -115,6 +115,8 @@ def test_prefill_validation():
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_offsets is NULL" in msg
     st, msg = _prefill(num_export=-1, export_grid=64)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "num_export_states" in msg
+    st, msg = _prefill(init_slot=FAKE, export_grid=64, num_export=4, export_slots=FAKE + 2)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_slots" in msg
     st, msg = _prefill(export_grid=1088)          # lcm(64, 1088) = 1088 is accepted; the NULL init_slot is not
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "init_slot is NULL" in msg
     st, msg = _prefill(num_seqs=0, q=None, cu=None)   # no sequences: a no-op
@@ -126,15 +128,15 @@ def test_mixed_step_validation():
     shape = B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
     # decode part checked first: slot_out NULL
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, None, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, 0, FAKE, 0, None)
+                            FAKE, FAKE, 8, FAKE, FAKE, None, 0, None, None, None, 0, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "slot_out is NULL" in B.gdn_last_error()
     # prefill part: export grid off the chunk grid (init_slot NULL as the guard)
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, None, FAKE, None, 100, FAKE, FAKE, 1, FAKE, 0, None)
+                            FAKE, FAKE, 8, None, FAKE, None, 100, FAKE, FAKE, None, 1, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "export_grid 100" in B.gdn_last_error()
     # prefill part: a NULL init_slot
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, None, FAKE, None, 0, None, None, 0, FAKE, 0, None)
+                            FAKE, FAKE, 8, None, FAKE, None, 0, None, None, None, 0, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "init_slot is NULL" in B.gdn_last_error()
 
 

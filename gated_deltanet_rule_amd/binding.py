@@ -50,6 +50,8 @@ SIGNATURES = {
     "gdn_mixed_step": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                       _i64, _vp, _sz, _vp]),
+    "gdn_recurrent_verify": (ctypes.c_int, [ctypes.POINTER(GdnShape), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _i32, _vp, _vp, _vp]),
     "gdn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -178,6 +180,23 @@ def gdn_recurrent_decode(q, k, v, g, beta, o, state_pool, slot_in, slot_out, *, 
         _check(library().gdn_recurrent_decode(
             ctypes.byref(shape), B, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
             _ptr(state_pool), num_slots, _ptr(slot_in), _ptr(slot_out), _stream(dev, stream)))
+
+
+def gdn_recurrent_verify(q, k, v, g, beta, o, state_pool, slot_in, token_slots, *, scale: float,
+                         tokens_per_row: int, stream=None) -> None:
+    """Multi-token verify rows: len(slot_in) rows of tokens_per_row tokens each, the
+    state after every token written to its token slot (see include/gdn.h)."""
+    B = slot_in.shape[0]
+    n = B * int(tokens_per_row)
+    dev, H_k, H_v, d_k, d_v = _heads(q, k, v, g, beta, o, n)
+    num_slots = _pool(state_pool, dev, H_v, d_k, d_v)
+    _index(slot_in, "slot_in", B, dev)
+    _index(token_slots, "token_slots", n, dev)
+    shape = make_shape(H_k, H_v, d_k, d_v, _dtype_code(q), scale)
+    with torch.cuda.device(dev):
+        _check(library().gdn_recurrent_verify(
+            ctypes.byref(shape), B, int(tokens_per_row), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+            _ptr(state_pool), num_slots, _ptr(slot_in), _ptr(token_slots), _stream(dev, stream)))
 
 
 def _prefill_common(dev, num_seqs, cu_seqlens, init_slot, final_slot, start_pos, export_grid,

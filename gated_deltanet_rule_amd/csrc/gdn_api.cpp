@@ -158,6 +158,7 @@ gdn::DecodeArgs decode_args(const gdn_shape* s, int32_t num_rows, const void* q,
     a.dtype = s->dtype;
     a.scale = s->scale;
     a.num_rows = num_rows;
+    a.tokens_per_row = 1;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -295,6 +296,24 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows, const
                                                        export_slots, num_export_states, workspace),
                                           stream),
                       "mixed-step prefill launch");
+}
+
+gdn_status gdn_recurrent_verify(const gdn_shape* shape, int32_t num_rows, int32_t tokens_per_row,
+                                const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                void* o, float* state_pool, int32_t num_slots, const int32_t* slot_in,
+                                const int32_t* token_slots, hipStream_t stream) {
+    g_last_error.clear();
+    if (tokens_per_row < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "tokens_per_row %d is less than 1", tokens_per_row);
+    if ((int64_t)num_rows * tokens_per_row > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "num_rows %d x tokens_per_row %d is too large", num_rows, tokens_per_row);
+    gdn_status st = check_decode(shape, num_rows, q, k, v, g, beta, o, state_pool, num_slots, slot_in,
+                                 token_slots);
+    if (st != GDN_OK || num_rows == 0) return st;
+    gdn::DecodeArgs a = decode_args(shape, num_rows, q, k, v, g, beta, o, state_pool, num_slots, slot_in,
+                                    token_slots);
+    a.tokens_per_row = tokens_per_row;
+    return hip_status(gdn::launch_decode(a, stream), "verify launch");
 }
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }

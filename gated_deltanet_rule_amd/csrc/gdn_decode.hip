@@ -1,11 +1,13 @@
-// gdn_decode.hip -- packed single-token recurrent decode for gfx950 (MI355X).
+// gdn_decode.hip -- packed recurrent decode for gfx950 (MI355X).
 //
 // One workgroup of 1024 threads advances the state of one (row, value head) by one
 // token ("[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
-// sections "Why" and "How": cached rows take the packed recurrent decode path).
-// The work is bound by HBM: each state (d_k x d_v fp32, 64 KiB at d = 128) is read
-// once and written once, so the kernel streams it with 16-byte coalesced loads into
-// registers, does the whole update there, and streams it back:
+// sections "Why" and "How": cached rows take the packed recurrent decode path), or by
+// tokens_per_row tokens in order for a multi-token verify row: the state stays in
+// registers between the row's tokens and is written after each token to that token's
+// slot.  The work is bound by HBM: each state (d_k x d_v fp32, 64 KiB at d = 128) is
+// read once and written once per kept token, so the kernel streams it with 16-byte
+// coalesced loads into registers, does the whole update there, and streams it back:
 //
 //     S <- exp(g) S;   u = beta (v - S^T k);   S <- S + k u^T;   o = scale S^T q
 //
@@ -14,10 +16,11 @@
 // rows r, r + RG, r + 2 RG, ...  Large workgroups keep few state rows per thread, so
 // two workgroups fit on a compute unit and the later ones' loads overlap the earlier
 // ones' stores (a cold in-place update of 64 KiB states runs at the speed of a plain
-// read-modify-write of the same blocks).  The two reductions over d_k (S^T k and S^T q) are
-// per-thread partial sums followed by a fixed-order sum over the row groups through
-// LDS, so the result does not depend on anything but the row's own data: a row's
-// output and state are bitwise the same in any batch, at any position.
+// read-modify-write of the same blocks).  The two reductions over d_k (S^T k and
+// S^T q) are per-thread partial sums followed by a fixed-order sum over the row groups
+// through LDS, so the result does not depend on anything but the row's own data: a
+// row's output and state are bitwise the same in any batch, at any position, and a
+// verify row equals the same tokens decoded one call at a time.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -93,12 +96,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int tid = threadIdx.x;
     const int c4 = tid % TPR;
     const int rg = tid / TPR;
+    const int NTOK = a.tokens_per_row;
 
     const int sin = a.slot_in[b];
-    const int sout = a.slot_out[b];
-    T* o = static_cast<T*>(a.o) + ((size_t)b * a.H_v + h) * DV;
     if (sin < 0 || sin >= a.num_slots) {          // padding row
-        if (tid < DV) o[tid] = from_f32<T>(0.f);
+        for (int t = 0; t < NTOK; ++t) {
+            T* o = static_cast<T*>(a.o) + ((size_t)(b * NTOK + t) * a.H_v + h) * DV;
+            if (tid < DV) o[tid] = from_f32<T>(0.f);
+        }
         return;
     }
 
@@ -111,63 +116,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     __shared__ float kq[2][DK];
     __shared__ float4 red[2][RG][TPR];
-    const T* kp = static_cast<const T*>(a.k) + ((size_t)b * a.H_k + kh) * DK;
-    const T* qp = static_cast<const T*>(a.q) + ((size_t)b * a.H_k + kh) * DK;
-    if (tid < DK) kq[0][tid] = to_f32(kp[tid]);
-    else if (tid < 2 * DK) kq[1][tid - DK] = to_f32(qp[tid - DK]);
-    const float4 vv = load4<T>(static_cast<const T*>(a.v) + ((size_t)b * a.H_v + h) * DV + 4 * c4);
-    const float alpha = expf(a.g[(size_t)b * a.H_v + h]);
-    const float beta = a.beta[(size_t)b * a.H_v + h];
-    __syncthreads();
+    // The row's tokens in order, the state kept in registers between them.  Every
+    // LDS array is rewritten only after the barrier that follows its last read.
+    for (int t = 0; t < NTOK; ++t) {
+        const size_t row = (size_t)b * NTOK + t;
+        T* o = static_cast<T*>(a.o) + (row * a.H_v + h) * DV;
+        const T* kp = static_cast<const T*>(a.k) + (row * a.H_k + kh) * DK;
+        const T* qp = static_cast<const T*>(a.q) + (row * a.H_k + kh) * DK;
+        if (tid < DK) kq[0][tid] = to_f32(kp[tid]);
+        else if (tid < 2 * DK) kq[1][tid - DK] = to_f32(qp[tid - DK]);
+        const float4 vv = load4<T>(static_cast<const T*>(a.v) + row * a.H_v * DV + (size_t)h * DV + 4 * c4);
+        const float alpha = expf(a.g[row * a.H_v + h]);
+        const float beta = a.beta[row * a.H_v + h];
+        __syncthreads();
 
-    // decay, then the partial prediction S^T k over this thread's rows
-    float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+        // decay, then the partial prediction S^T k over this thread's rows
+        float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int m = 0; m < R; ++m) {
-        s[m].x *= alpha; s[m].y *= alpha; s[m].z *= alpha; s[m].w *= alpha;
-        const float kr = kq[0][rg + RG * m];
-        p.x = fmaf(s[m].x, kr, p.x); p.y = fmaf(s[m].y, kr, p.y);
-        p.z = fmaf(s[m].z, kr, p.z); p.w = fmaf(s[m].w, kr, p.w);
-    }
-    red[0][rg][c4] = p;
-    __syncthreads();
-    float4 tot = red[0][0][c4];
-#pragma unroll
-    for (int r = 1; r < RG; ++r) {
-        const float4 x = red[0][r][c4];
-        tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
-    }
-    const float4 u = make_float4(beta * (vv.x - tot.x), beta * (vv.y - tot.y),
-                                 beta * (vv.z - tot.z), beta * (vv.w - tot.w));
-
-    // rank-1 write, then the partial read S^T q from the updated state
-    float4 po = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-        const float kr = kq[0][rg + RG * m];
-        const float qr = kq[1][rg + RG * m];
-        s[m].x = fmaf(kr, u.x, s[m].x); s[m].y = fmaf(kr, u.y, s[m].y);
-        s[m].z = fmaf(kr, u.z, s[m].z); s[m].w = fmaf(kr, u.w, s[m].w);
-        po.x = fmaf(s[m].x, qr, po.x); po.y = fmaf(s[m].y, qr, po.y);
-        po.z = fmaf(s[m].z, qr, po.z); po.w = fmaf(s[m].w, qr, po.w);
-    }
-    if (sout >= 0 && sout < a.num_slots) {
-        float* dst = a.pool + ((size_t)sout * a.H_v + h) * (size_t)(DK * DV);
-#pragma unroll
-        for (int m = 0; m < R; ++m)
-            store_state(dst + (size_t)(rg + RG * m) * DV + 4 * c4, s[m]);
-    }
-    red[1][rg][c4] = po;
-    __syncthreads();
-    if (rg == 0) {
-        float4 to = red[1][0][c4];
+        for (int m = 0; m < R; ++m) {
+            s[m].x *= alpha; s[m].y *= alpha; s[m].z *= alpha; s[m].w *= alpha;
+            const float kr = kq[0][rg + RG * m];
+            p.x = fmaf(s[m].x, kr, p.x); p.y = fmaf(s[m].y, kr, p.y);
+            p.z = fmaf(s[m].z, kr, p.z); p.w = fmaf(s[m].w, kr, p.w);
+        }
+        red[0][rg][c4] = p;
+        __syncthreads();
+        float4 tot = red[0][0][c4];
 #pragma unroll
         for (int r = 1; r < RG; ++r) {
-            const float4 x = red[1][r][c4];
-            to.x += x.x; to.y += x.y; to.z += x.z; to.w += x.w;
+            const float4 x = red[0][r][c4];
+            tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
         }
-        const float sc = a.scale;
-        store4<T>(o + 4 * c4, make_float4(sc * to.x, sc * to.y, sc * to.z, sc * to.w));
+        const float4 u = make_float4(beta * (vv.x - tot.x), beta * (vv.y - tot.y),
+                                     beta * (vv.z - tot.z), beta * (vv.w - tot.w));
+
+        // rank-1 write, then the partial read S^T q from the updated state
+        float4 po = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const float kr = kq[0][rg + RG * m];
+            const float qr = kq[1][rg + RG * m];
+            s[m].x = fmaf(kr, u.x, s[m].x); s[m].y = fmaf(kr, u.y, s[m].y);
+            s[m].z = fmaf(kr, u.z, s[m].z); s[m].w = fmaf(kr, u.w, s[m].w);
+            po.x = fmaf(s[m].x, qr, po.x); po.y = fmaf(s[m].y, qr, po.y);
+            po.z = fmaf(s[m].z, qr, po.z); po.w = fmaf(s[m].w, qr, po.w);
+        }
+        const int sout = a.slot_out[row];
+        if (sout >= 0 && sout < a.num_slots) {
+            float* dst = a.pool + ((size_t)sout * a.H_v + h) * (size_t)(DK * DV);
+#pragma unroll
+            for (int m = 0; m < R; ++m)
+                store_state(dst + (size_t)(rg + RG * m) * DV + 4 * c4, s[m]);
+        }
+        red[1][rg][c4] = po;
+        __syncthreads();
+        if (rg == 0) {
+            float4 to = red[1][0][c4];
+#pragma unroll
+            for (int r = 1; r < RG; ++r) {
+                const float4 x = red[1][r][c4];
+                to.x += x.x; to.y += x.y; to.z += x.z; to.w += x.w;
+            }
+            const float sc = a.scale;
+            store4<T>(o + 4 * c4, make_float4(sc * to.x, sc * to.y, sc * to.z, sc * to.w));
+        }
     }
 }
 

@@ -8,11 +8,13 @@
 
 namespace gdn {
 
-// Packed single-token decode over cached rows.
+// Packed decode over cached rows: tokens_per_row tokens per row (1 for decode,
+// more for verify rows); slot_out holds one slot per token.
 struct DecodeArgs {
     int H_k, H_v, d_k, d_v, dtype;
     float scale;
     int num_rows;
+    int tokens_per_row;
     const void* q;
     const void* k;
     const void* v;

@@ -202,6 +202,36 @@ gdn_status gdn_mixed_step(const gdn_shape* shape, int32_t num_decode_rows,
                           int64_t num_export_states, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * Multi-token verify rows: each of num_rows cached rows advances by tokens_per_row
+ * tokens in order, as tokens_per_row successive decode steps of that row, and the state
+ * after each token is kept so that a caller can roll the row back to any accepted
+ * prefix of the tokens.
+ *   Context: speculative decoding is left out of the mixed-step route ("[Model] Enable
+ *   batch-invariant mixed decode and prefill for Qwen GDN", section "Out of scope") and
+ *   of prefix caching ("[V1][Hybrid] GatedDeltaNet Automatic Prefix Caching", section
+ *   "TODOs"); this is the recurrent path such rows would take.
+ *   q, k       device [num_rows * tokens_per_row, num_k_heads, d_k]: row b's tokens are
+ *              rows b * tokens_per_row .. b * tokens_per_row + tokens_per_row - 1.
+ *   v, o       device [num_rows * tokens_per_row, num_v_heads, d_v] (o written).
+ *   g, beta    device [num_rows * tokens_per_row, num_v_heads] fp32.
+ *   slot_in    device [num_rows] int32: the row's state before its first token; a slot
+ *              outside [0, num_slots) marks a padding row (outputs zero-filled, no state
+ *              written).
+ *   token_slots device [num_rows * tokens_per_row] int32: the state after token t of
+ *              row b is written to state_pool[token_slots[b * tokens_per_row + t]];
+ *              a slot outside [0, num_slots) keeps that state nowhere.  A token slot may
+ *              equal slot_in (then the state is read before any write).
+ *   With tokens_per_row = 1 this is gdn_recurrent_decode (token_slots = slot_out), on
+ *   the same kernel; a verify row is bitwise equal to its tokens decoded one call at a
+ *   time.  tokens_per_row < 1 returns GDN_ERR_INVALID_ARGUMENT.
+ */
+gdn_status gdn_recurrent_verify(const gdn_shape* shape, int32_t num_rows, int32_t tokens_per_row,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, void* o, float* state_pool, int32_t num_slots,
+                                const int32_t* slot_in, const int32_t* token_slots,
+                                hipStream_t stream);
+
 /* Message describing the last non-OK status returned on the calling thread ("" if
  * none).  The pointer stays valid until the thread's next call into the library. */
 const char* gdn_last_error(void);

@@ -29,7 +29,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"gdn_chunk_prefill_workspace_size", "gdn_recurrent_decode", "gdn_chunk_prefill",
-                          "gdn_mixed_step", "gdn_last_error"}
+                          "gdn_mixed_step", "gdn_recurrent_verify", "gdn_last_error"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -138,6 +138,20 @@ def test_mixed_step_validation():
     st = lib.gdn_mixed_step(ctypes.byref(shape), 3, FAKE, FAKE, 1, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE, 8, None, FAKE, None, 0, None, None, None, 0, FAKE, 0, None)
     assert st == B.GDN_ERR_INVALID_ARGUMENT and "init_slot is NULL" in B.gdn_last_error()
+
+
+def test_verify_validation():
+    lib = B.library()
+    shape = B.make_shape(2, 4, 64, 64, B.GDN_BF16, 0.125)
+    st = lib.gdn_recurrent_verify(ctypes.byref(shape), 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE,
+                                  FAKE, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "tokens_per_row 0" in B.gdn_last_error()
+    st = lib.gdn_recurrent_verify(ctypes.byref(shape), 3, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE,
+                                  None, None)
+    assert st == B.GDN_ERR_INVALID_ARGUMENT and "is NULL" in B.gdn_last_error()
+    st = lib.gdn_recurrent_verify(ctypes.byref(shape), 0, 4, None, None, None, None, None, None, None, 0, None,
+                                  None, None)
+    assert st == B.GDN_OK                          # no rows: a no-op
 
 
 def test_binding_checks_tensors_before_calling():

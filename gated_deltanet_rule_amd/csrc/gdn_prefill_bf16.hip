@@ -192,7 +192,11 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     const int hh = wv / NWH;                 // this wave's head within the group
     const int h = h0 + hh;
     const int col0 = 32 * (wv - hh * NWH);
-    const bool lead = wv == hh * NWH;        // first wave of its head
+    // The "first" wave of each head (the one that scans the gates and inverts the
+    // diagonal blocks) is wave hh of the head, so that the heads' first waves sit on
+    // different SIMDs (waves go to SIMDs by index modulo 4).
+    const int wi = wv - hh * NWH;            // wave index within the head
+    const bool lead = wi == hh % NWH;
     typename SM::Head& hd = sm.hd[hh];
 
     const size_t SE = (size_t)DK * DV;
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
         } else {
             constexpr int NTI = (16 + NNL - 1) / NNL;
-            const int nl = wv - hh - 1;          // index among the waves that are not first
+            const int nl = hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);   // index among the others
 #pragma unroll
             for (int n = 0; n < NTI; ++n) {
                 const int tt = nl + NNL * n;     // wave-uniform: 0..5 K K^T, 6..15 Q K^T

@@ -535,9 +535,23 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
+                // blocks j in pairs on 16x16x32 (the pair's U registers side by side are
+                // the from-C operand), a last odd block on 16x16x16
                 f32x4 X = Racc[i][nt];
 #pragma unroll
-                for (int j = 0; j < i; ++j) {
+                for (int j = 0; j + 1 < i; j += 2) {
+                    const bf16x8 ah = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
+                                           ld4(hd.sol[blk(i, j + 1)][0] + li * SM::BLD + 4 * g4));
+                    const bf16x8 al = cat8(ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4),
+                                           ld4(hd.sol[blk(i, j + 1)][1] + li * SM::BLD + 4 * g4));
+                    const bf16x8 uh = cat8(Us[j][nt].hi, Us[j + 1][nt].hi);
+                    const bf16x8 ul = cat8(Us[j][nt].lo, Us[j + 1][nt].lo);
+                    X = mma32(ah, uh, X);
+                    X = mma32(ah, ul, X);
+                    X = mma32(al, uh, X);
+                }
+                if (i & 1) {
+                    const int j = i - 1;
                     const bf16x4 ah = ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4);
                     const bf16x4 al = ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4);
                     X = mma16(ah, Us[j][nt].hi, X);

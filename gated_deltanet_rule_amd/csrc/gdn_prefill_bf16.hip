@@ -23,17 +23,21 @@
 // for the whole sequence.  The d_v columns of S, R, U and O are independent, so
 // strips never exchange data.  The solve runs on 16-row blocks of the chunk:
 //     U_i = T_ii (R_i - sum_{j<i} A_ij U_j),   T_ii = (I + A_ii)^-1 (16 x 16)
-// Per chunk, with three workgroup barriers:
-//   stage    the previous chunk's prefetched Q, K (also transposed) and V rows go to
-//            LDS; the first wave of each head scans the gates from its registers
-//   phase 1  lower 16x16 tiles of K K^T and Q K^T (shared by the HG heads), turned
-//            into -A_ij blocks, fp32 A_ii blocks and P blocks per head; then, per
-//            strip, Z = K S and Q S on MFMA and R = beta (V - gamma Z), V entering
-//            the accumulators through an identity product
-//   phase 2  the first wave of each head inverts the four A_ii blocks by forward
-//            substitution (lane 16b + j owns column j of block b)
+// Per chunk, with two workgroup barriers:
+//   phase 1  the first wave of each head forms its head's four diagonal K K^T tiles
+//            and inverts I + A_ii by forward substitution (lane 16b + j owns column
+//            j of block b); the other waves form the sixteen shared lower tiles of
+//            K K^T and Q K^T (the HG heads share k and q) and turn them into the
+//            -A_ij blocks and the P blocks (scale folded in) of every head.  Then,
+//            per strip, Z = K S and Q S on MFMA and R = beta (V - gamma Z), V
+//            entering the accumulators through an identity product
+//   stage    after the first barrier, the next chunk's prefetched Q, K and V rows
+//            go to LDS (K and the gates by chunk parity), the first wave of each
+//            head scans the next gates from its registers, and the chunk after
+//            that is fetched into registers
 //   phase 3  per strip: the block solve for U, each output row block as soon as
-//            its U blocks exist, then the state update and the grid export
+//            its U blocks exist, then the state update (K^T read from the K rows
+//            by transposing LDS reads) and the grid export
 // Precision.  All products are bf16 MFMA with fp32 accumulation.  q, k and v enter
 // exactly; S, Z and P enter as single bf16 values; every operand the solve and the
 // state update depend on -- the -A_ij and T_ii blocks, the right-hand sides, U and
@@ -106,6 +110,16 @@ __device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cas
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ void st4(__bf16* p, bf16x4 x) { *reinterpret_cast<bf16x4*>(p) = x; }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// 16 g + i receives element e = 0..3 from the address of lane 16 g + 4 e + i / 4, at
+// position i % 4 of that lane's four values.  So if lane l points at row r0 + l / 4,
+// columns c0 + 4 (l % 4) of a row-major bf16 matrix M, lane 16 g + i gets
+// M[r0 + 4 g + e][c0 + i]: the A operand of M^T (row i, k = 4 g + e) in one read.
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ bf16x4 ld4_tr(const __bf16* p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
 // 16x32 operand of a row-major LDS row, k from 32 ks in from-C order
 __device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g) {
     return cat8(ld4(row + 32 * ks + 4 * g), ld4(row + 32 * ks + 16 + 4 * g));
@@ -131,17 +145,14 @@ enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, kGates = 4 };
 template <int DK, int DV, int HG>
 struct Smem {
     static constexpr int QLD = DK + 8;        // Q and K rows (bf16)
-    static constexpr int KTLD = kC + 8;       // K^T rows (bf16)
     static constexpr int VLD = DV + 8;        // V rows (bf16)
     static constexpr int BLD = 20;            // rows of a 16x16 bf16 block
     static constexpr int BSZ = 16 * BLD;
     static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
     static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
     __bf16 q[kC * QLD];
-    __bf16 k[kC * QLD];
-    __bf16 kt[2][DK * KTLD];                  // K^T, by chunk parity (the state update of
-                                              // chunk c reads it while chunk c+1 is staged);
-                                              // row d holds token group q at group q ^ (d / 16)
+    __bf16 k[2][kC * QLD];                    // by chunk parity (the state update of chunk
+                                              // c reads it while chunk c+1 is staged)
     struct Head {
         __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
@@ -291,32 +302,26 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             pv[j] = (int)r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    // Write chunk c's prefetched Q and K rows, K^T and the gates (those two by chunk
-    // parity) to LDS.  For chunk c + 1 this runs right after the barrier that ends
-    // phase 1 of chunk c: Q and K were last read in phase 1, and the other parity of
-    // K^T and the gates was last read in phase 3 of chunk c - 1.  Doing it before
-    // phase 3 issues its stores keeps the wait for the loads from waiting for those.
+    // Write chunk c's prefetched Q and K rows and the gates (those two by chunk parity)
+    // to LDS.  For chunk c + 1 this runs right after the barrier that ends phase 1 of
+    // chunk c: Q was last read in phase 1, and the other parity of K and the gates was
+    // last read in phase 3 of chunk c - 1.  Doing it before phase 3 issues its stores
+    // keeps the wait for the loads from waiting for those.
     auto stage_qk = [&](int c, unsigned t) {
-        const int buf = c & 1;
-        __bf16* kt = sm.kt[buf];
+        __bf16* kb = sm.k[c & 1];
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const unsigned i = t + NT * j;
             const unsigned r = i / VPR, vi = i % VPR;
             *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + vi * 8) = pq[j];
-            *reinterpret_cast<uint4*>(sm.k + r * SM::QLD + vi * 8) = pk[j];
-            // K^T row d = 8 vi + e; token groups of four swizzled by d / 16 = vi / 2
-            const bf16x8 x = __builtin_bit_cast(bf16x8, pk[j]);
-            const unsigned col = 4 * ((r >> 2) ^ (vi >> 1)) + (r & 3);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kt[(vi * 8 + e) * SM::KTLD + col] = x[e];
+            *reinterpret_cast<uint4*>(kb + r * SM::QLD + vi * 8) = pk[j];
         }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
             const int ln = t & 63;
             const float G2 = dev::wave_inclusive_sum(gpf * kLog2e);
             const float G2_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G2), kC - 1));
-            float* gt = hd.gate[buf];
+            float* gt = hd.gate[c & 1];
             gt[GATE_G2 * kC + ln] = G2;
             gt[GATE_GAM * kC + ln] = __builtin_amdgcn_exp2f(G2);
             gt[GATE_BET * kC + ln] = bpf;
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         int tid_l = tid;
         asm volatile("" : "+v"(lane), "+v"(tid_l));
         const int li = lane & 15, g4 = lane >> 4;
-        __bf16* kt = sm.kt[buf];
+        const __bf16* kb = sm.k[buf];
 
         dev::lds_barrier();
 
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             for (int b = 0; b < 4; ++b) {
                 bf16x8 kf[KS_DK];             // both operands are this block's K rows
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(sm.k + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4);
+                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(kb + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(kf[kk], kf[kk], acc);
@@ -436,11 +441,11 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 } else {
                     tile_ij(tt - 6, i, j);
                 }
-                const __bf16* X = tt < 6 ? sm.k : sm.q;
+                const __bf16* X = tt < 6 ? kb : sm.q;
                 bf16x8 fa[KS_DK], fb[KS_DK];
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    fa[kk] = ld8(sm.k + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4);
+                    fa[kk] = ld8(kb + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4);
                     fb[kk] = ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4);
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    const bf16x8 ak = row_fromc(sm.k + (16 * mt + li) * SM::QLD, kk, g4);
+                    const bf16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4);
                     const bf16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
@@ -600,10 +605,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         }
 
         // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs.  The B operands
-        // first; then the K^T reads run two steps ahead of the MFMAs that use them.
-        const __bf16* krow[4];                // this lane's K^T row li, swizzle part g4 ^ m
-#pragma unroll
-        for (int m = 0; m < 4; ++m) krow[m] = kt + li * SM::KTLD + 4 * (g4 ^ m);
+        // first; then the K^T reads (transposing reads of the K rows) run two steps
+        // ahead of the MFMAs that use them.
+        const __bf16* ktr = kb + (lane >> 2) * SM::QLD + 4 * (lane & 3);
         bf16x8 bh[2][2], bl[2][2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -617,12 +621,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 bl[kk][nt] = cat8(s0.lo, s1.lo);
             }
         }
-        // step t = (mt, kk) = (t / 2, t % 2); row d = 16 mt + li, token groups
-        // (8 kk + 4 h + g4) ^ mt = (8 kk + 4 (h ^ mt / 4)) + (g4 ^ mt % 4)
+        // step t = (mt, kk) = (t / 2, t % 2): K^T rows d = 16 mt + li, tokens
+        // 32 kk + 4 g4 + e and 32 kk + 16 + 4 g4 + e (the from-C order)
         auto kfrag = [&](int t) {
             const int mt = t >> 1, kk = t & 1;
-            const __bf16* kr = krow[mt & 3] + 16 * mt * SM::KTLD;
-            return cat8(ld4(kr + 4 * (8 * kk + 4 * (0 ^ (mt >> 2)))), ld4(kr + 4 * (8 * kk + 4 * (1 ^ (mt >> 2)))));
+            const __bf16* kr = ktr + 32 * kk * SM::QLD + 16 * mt;
+            return cat8(ld4_tr(kr), ld4_tr(kr + 16 * SM::QLD));
         };
         __builtin_amdgcn_sched_barrier(0);
         {

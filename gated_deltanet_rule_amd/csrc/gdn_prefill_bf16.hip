@@ -86,13 +86,25 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // x = hi + lo: hi rounded to bf16, lo the exact remainder rounded once (two values
-// per conversion instruction)
+// per conversion instruction).  The remainder x - hi comes from one bf16 dot product
+// per value, hi . (-1, 0) + x or hi . (0, -1) + x, which is exact (the true result is
+// representable) and saves widening hi back to fp32 first.  The two packed (-1, 0)
+// constants are made in SGPRs: left to the compiler they become inline constants,
+// and those did not read as the intended bf16 pairs.
 __device__ __forceinline__ Split4 split4(f32x4 x) {
     const f32x2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
     const bf16x2 h01 = __builtin_convertvector(x01, bf16x2);
     const bf16x2 h23 = __builtin_convertvector(x23, bf16x2);
-    const bf16x2 l01 = __builtin_convertvector(x01 - __builtin_convertvector(h01, f32x2), bf16x2);
-    const bf16x2 l23 = __builtin_convertvector(x23 - __builtin_convertvector(h23, f32x2), bf16x2);
+    unsigned c0, c1;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(c0));       // bf16 pair (-1, 0)
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(c1));   // bf16 pair (0, -1)
+    const bf16x2 m0 = __builtin_bit_cast(bf16x2, c0), m1 = __builtin_bit_cast(bf16x2, c1);
+    const f32x2 r01 = {__builtin_amdgcn_fdot2_f32_bf16(h01, m0, x[0], false),
+                       __builtin_amdgcn_fdot2_f32_bf16(h01, m1, x[1], false)};
+    const f32x2 r23 = {__builtin_amdgcn_fdot2_f32_bf16(h23, m0, x[2], false),
+                       __builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false)};
+    const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
+    const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
     Split4 s;
     s.hi = bf16x4{h01[0], h01[1], h23[0], h23[1]};
     s.lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
@@ -120,9 +132,11 @@ __device__ __forceinline__ bf16x4 ld4_tr(const __bf16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
-// 16x32 operand of a row-major LDS row, k from 32 ks in from-C order
-__device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g) {
-    return cat8(ld4(row + 32 * ks + 4 * g), ld4(row + 32 * ks + 16 + 4 * g));
+// 16x32 operand of a row-major Q or K row in LDS, k from 32 ks in from-C order; sw is
+// the row's column swizzle (see Smem)
+__device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g, int sw) {
+    const __bf16* p = row + ((4 * g) ^ sw);    // the swizzle only touches column bit 3
+    return cat8(ld4(p + 32 * ks), ld4(p + 32 * ks + 16));
 }
 
 // B operand (from-C order, k step ks) out of a pair of state accumulator tiles
@@ -144,9 +158,16 @@ enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, kGates = 4 };
 
 template <int DK, int DV, int HG>
 struct Smem {
-    static constexpr int QLD = DK + 8;        // Q and K rows (bf16)
+    // Q and K rows (bf16).  The pitch is an odd multiple of 8 dwords and row r keeps
+    // its 16-byte column groups swizzled, column c at c ^ (r & 8): with that, the
+    // row-fragment reads (16 rows, one column group each), the transposing reads
+    // (8 rows x 32 bytes per half wave) and the staging writes all hit distinct
+    // banks.
+    static constexpr int QLD = DK + 16;
     static constexpr int VLD = DV + 8;        // V rows (bf16)
-    static constexpr int BLD = 20;            // rows of a 16x16 bf16 block
+    static constexpr int BLD = 24;            // rows of a 16x16 bf16 block (12 dwords:
+                                              // a half wave's 8-byte row reads are
+                                              // bank-conflict free)
     static constexpr int BSZ = 16 * BLD;
     static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
     static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
@@ -157,8 +178,7 @@ struct Smem {
         __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
         __bf16 p[10][BSZ];                    // P blocks
-        float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s];
-                                              // in phase 3 the output staging of the head's waves
+        float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
         float gate[2][kGates * kC];           // by chunk parity
     } hd[HG];
 };
@@ -313,8 +333,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         for (int j = 0; j < NQ; ++j) {
             const unsigned i = t + NT * j;
             const unsigned r = i / VPR, vi = i % VPR;
-            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + vi * 8) = pq[j];
-            *reinterpret_cast<uint4*>(kb + r * SM::QLD + vi * 8) = pk[j];
+            const unsigned col = (vi * 8) ^ (r & 8);
+            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = pq[j];
+            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = pk[j];
         }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             for (int b = 0; b < 4; ++b) {
                 bf16x8 kf[KS_DK];             // both operands are this block's K rows
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(kb + (16 * b + li) * SM::QLD + 32 * kk + 8 * g4);
+                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(kb + (16 * b + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(kf[kk], kf[kk], acc);
@@ -445,8 +466,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 bf16x8 fa[KS_DK], fb[KS_DK];
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    fa[kk] = ld8(kb + (16 * j + li) * SM::QLD + 32 * kk + 8 * g4);
-                    fb[kk] = ld8(X + (16 * i + li) * SM::QLD + 32 * kk + 8 * g4);
+                    fa[kk] = ld8(kb + (16 * j + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
+                    fb[kk] = ld8(X + (16 * i + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -477,7 +498,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
         }
 
-        // this strip's Z = K S and Q S; R = beta (V - gamma Z); S scaled by gamma_last
+        // this strip's Z = K S and (Q S)^T; R = beta (V - gamma Z); S scaled by gamma_last.
+        // O is accumulated transposed (value columns as rows), so that a lane ends up
+        // with four consecutive columns of one output row.
         const float* gt = hd.gate[buf];
         f32x4 Racc[4][2], Oacc[4][2];
         {
@@ -491,12 +514,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    const bf16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4);
-                    const bf16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4);
+                    const bf16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
+                    const bf16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         Racc[mt][nt] = mma32(ak, Sb[kk][nt], Racc[mt][nt]);
-                        Oacc[mt][nt] = mma32(aq, Sb[kk][nt], Oacc[mt][nt]);
+                        Oacc[mt][nt] = mma32(Sb[kk][nt], aq, Oacc[mt][nt]);
                     }
                 }
             }
@@ -510,9 +533,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         for (int mt = 0; mt < 4; ++mt) {
             const f32x4 gam = *reinterpret_cast<const f32x4*>(gt + GATE_GAM * kC + 16 * mt + 4 * g4);
             const f32x4 bet = *reinterpret_cast<const f32x4*>(gt + GATE_BET * kC + 16 * mt + 4 * g4);
+            const float sg = a.scale * gt[GATE_GAM * kC + 16 * mt + li];   // output row 16 mt + li
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                Oacc[mt][nt] *= a.scale * gam;
+                Oacc[mt][nt] *= sg;
                 // + V through V I, onto -gamma Z
                 const bf16x4 av = ld4(hd.v + (16 * mt + li) * SM::VLD + col0 + 16 * nt + 4 * g4);
                 Racc[mt][nt] = mma16(av, ident, -gam * Racc[mt][nt]);
@@ -532,9 +556,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
-        constexpr int OLD = 40;                                        // O staging rows (bf16)
-        static_assert(NWH * 16 * OLD * 2 <= 4 * SM::ATB * 4, "output staging must fit the A_ii space");
-        __bf16* oslot = reinterpret_cast<__bf16*>(hd.at) + (wv - hh * NWH) * 16 * OLD;
         Split4 Us[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -572,7 +593,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[i][nt] = U;
                 Us[i][nt] = split4(U);
             }
-            // O rows 16 i .. 16 i + 15: + P_i,(0..i) U_(0..i), blocks in pairs
+            // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, blocks in pairs
             const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
@@ -584,30 +605,32 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 for (int nt = 0; nt < 2; ++nt) {
                     const bf16x4 h1 = j1 <= i ? Us[j1][nt].hi : z4;
                     const bf16x4 l1 = j1 <= i ? Us[j1][nt].lo : z4;
-                    Oacc[i][nt] = mma32(pa, cat8(Us[j0][nt].hi, h1), Oacc[i][nt]);
-                    Oacc[i][nt] = mma32(pa, cat8(Us[j0][nt].lo, l1), Oacc[i][nt]);
+                    Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, h1), pa, Oacc[i][nt]);
+                    Oacc[i][nt] = mma32(cat8(Us[j0][nt].lo, l1), pa, Oacc[i][nt]);
                 }
             }
-            // out through LDS (this wave's slot in its head's A_ii space, unused in phase 3):
-            // one 16-byte store per lane per row block
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    oslot[(4 * g4 + e) * OLD + 16 * nt + li] = (__bf16)Oacc[i][nt][e];
+            // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap
+            // between lane groups g4 and g4 ^ 1 (v_permlane16_swap: rows 1 and 3 of the
+            // first register trade places with rows 0 and 2 of the second) leaves an
+            // even group with the nt = 0 columns 4 g4 .. 4 g4 + 7 and an odd group with
+            // the nt = 1 columns 12 + 4 g4 .. 12 + 4 g4 + 7: one 16-byte store per lane.
             {
-                const int row = lane >> 2, q = lane & 3;
-                const uint4 x = *reinterpret_cast<const uint4*>(oslot + row * OLD + 8 * q);
-                const int r = 16 * i + row;
-                const uint32_t off = (uint32_t)(r * a.H_v * DV + 8 * q) * 2u;
-                if (r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(obase) + off) = x;
+                const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][0], bf16x4));
+                const uint2 y = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][1], bf16x4));
+                const auto s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+                const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                const int r = 16 * i + li;
+                const int col = (g4 & 1) ? 12 + 4 * g4 : 4 * g4;
+                const uint32_t off = (uint32_t)(r * a.H_v * DV + col) * 2u;
+                if (r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(obase) + off) = w;
             }
         }
 
         // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs.  The B operands
         // first; then the K^T reads (transposing reads of the K rows) run two steps
         // ahead of the MFMAs that use them.
-        const __bf16* ktr = kb + (lane >> 2) * SM::QLD + 4 * (lane & 3);
+        const __bf16* ktr = kb + (lane >> 2) * SM::QLD + ((4 * (lane & 3)) ^ ((lane >> 2) & 8));
         bf16x8 bh[2][2], bl[2][2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {

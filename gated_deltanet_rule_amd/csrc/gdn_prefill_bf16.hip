@@ -562,7 +562,11 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 // blocks j in pairs on 16x16x32 (the pair's U registers side by side are
-                // the from-C operand), a last odd block on 16x16x16
+                // the from-C operand), a last odd block on 16x16x32 too, with a zero
+                // second half.  Every product that accumulates into X has one shape:
+                // back-to-back dependent MFMAs pass the accumulator on without wait
+                // states only between identical instructions, and the compiler does not
+                // pad a 16x16x32 -> 16x16x16 switch on the same registers.
                 f32x4 X = Racc[i][nt];
 #pragma unroll
                 for (int j = 0; j + 1 < i; j += 2) {
@@ -578,11 +582,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 }
                 if (i & 1) {
                     const int j = i - 1;
-                    const bf16x4 ah = ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4);
-                    const bf16x4 al = ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4);
-                    X = mma16(ah, Us[j][nt].hi, X);
-                    X = mma16(ah, Us[j][nt].lo, X);
-                    X = mma16(al, Us[j][nt].hi, X);
+                    const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                    const bf16x8 ah = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4), z4);
+                    const bf16x8 al = cat8(ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4), z4);
+                    X = mma32(ah, cat8(Us[j][nt].hi, z4), X);
+                    X = mma32(ah, cat8(Us[j][nt].lo, z4), X);
+                    X = mma32(al, cat8(Us[j][nt].hi, z4), X);
                 }
                 const Split4 xs = split4(X);
                 const bf16x4 th = ld4(hd.sol[blk(i, i)][0] + li * SM::BLD + 4 * g4);

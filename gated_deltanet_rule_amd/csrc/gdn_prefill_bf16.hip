@@ -154,7 +154,12 @@ __device__ __forceinline__ bf16x8 state_frag(const f32x4& t0, const f32x4& t1) {
 // Lower 16x16 blocks (i, j), j <= i, of a 64x64 matrix, numbered row by row.
 __device__ __forceinline__ constexpr int blk(int i, int j) { return i * (i + 1) / 2 + j; }
 
-enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, kGates = 4 };
+// Per-token gate tables of a chunk (one head): G2 = G log2(e) (inclusive cumsum of g in
+// base 2), GAM = e^G, BET = beta, KDEC = e^(G_last - G), FS = e^(G - G at the first token
+// of the token's 16-row block), TE = e^(G at the last token of the block - G).  For r in
+// block i and s in an earlier block j, e^(G_r - G_s) = FS_r e^(G_16i - G_16j+15) TE_s,
+// three factors of at most 1.
+enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, GATE_FS = 4, GATE_TE = 5, kGates = 6 };
 
 template <int DK, int DV, int HG>
 struct Smem {
@@ -342,11 +347,17 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             const int ln = t & 63;
             const float G2 = dev::wave_inclusive_sum(gpf * kLog2e);
             const float G2_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G2), kC - 1));
+            // G2 at the first and the last token of this lane's 16-token block (DPP
+            // row_newbcast:0 and :15; a row of 16 lanes is a block)
+            const float G2_bs = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, G2), 0x150, 0xf, 0xf, false));
+            const float G2_be = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, G2), 0x15f, 0xf, 0xf, false));
             float* gt = hd.gate[c & 1];
             gt[GATE_G2 * kC + ln] = G2;
             gt[GATE_GAM * kC + ln] = __builtin_amdgcn_exp2f(G2);
             gt[GATE_BET * kC + ln] = bpf;
             gt[GATE_KDEC * kC + ln] = __builtin_amdgcn_exp2f(G2_last - G2);
+            gt[GATE_FS * kC + ln] = __builtin_amdgcn_exp2f(G2 - G2_bs);
+            gt[GATE_TE * kC + ln] = __builtin_amdgcn_exp2f(G2_be - G2);
         }
     };
     // Chunk c's V rows to LDS (for chunk c + 1 right after phase 1 of chunk c, the
@@ -478,20 +489,27 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 for (int x = 0; x < HG; ++x) {
                     typename SM::Head& hx = sm.hd[x];
                     const float* gx = hx.gate[buf];
-                    const float G2r = gx[GATE_G2 * kC + r];
-                    const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
-                    f32x4 d;   // e^(G_r - G_s) where s <= r, else 1 (never used)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) d[e] = __builtin_amdgcn_exp2f(s0 + e <= r ? G2r - G2s[e] : 0.f);
-                    if (tt < 6) {                // strictly below the diagonal
-                        const float br = gx[GATE_BET * kC + r];
-                        const Split4 sp = split4(-(br * acc * d));
-                        st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
-                        st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
-                    } else {
+                    if (i != j) {
+                        // block (i, j) below the diagonal: e^(G_r - G_s) = FS_r c TE_s with
+                        // c = e^(G_16i - G_16j+15)
+                        const float c2 = gx[GATE_G2 * kC + 16 * i] - gx[GATE_G2 * kC + 16 * j + 15];
+                        const float fr = gx[GATE_FS * kC + r] * __builtin_amdgcn_exp2f(c2);
+                        const f32x4 te = *reinterpret_cast<const f32x4*>(gx + GATE_TE * kC + s0);
+                        if (tt < 6) {            // -A_ij = -beta_r (K K^T)_rs D_rs
+                            const Split4 sp = split4(acc * te * -(fr * gx[GATE_BET * kC + r]));
+                            st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                            st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                        } else {
+                            st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4,
+                                __builtin_convertvector(acc * te * (a.scale * fr), bf16x4));
+                        }
+                    } else {                     // a diagonal block of Q K^T: s <= r only
+                        const float G2r = gx[GATE_G2 * kC + r];
+                        const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
                         bf16x4 pv4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pv4[e] = (__bf16)(s0 + e <= r ? a.scale * acc[e] * d[e] : 0.f);
+                        for (int e = 0; e < 4; ++e)
+                            pv4[e] = (__bf16)(s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f);
                         st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
                     }
                 }

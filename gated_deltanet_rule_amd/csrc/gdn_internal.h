@@ -58,8 +58,6 @@ struct PrefillArgs {
 // Device scratch the prefill needs (none: every chunk's intermediates stay in LDS
 // and registers).
 size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_tokens);
-// Value heads that share one workgroup (and its staged Q and K).
-int prefill_heads_per_group(int dtype, int H_k, int H_v);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // The bf16 kernel (gdn_prefill_bf16.hip); launch_prefill routes bf16 calls to it.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

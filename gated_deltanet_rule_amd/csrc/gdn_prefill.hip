@@ -1,4 +1,6 @@
-// gdn_prefill.hip -- chunked prefill of the gated delta rule for gfx950 (MI355X).
+// gdn_prefill.hip -- chunked prefill of the gated delta rule for fp32 inputs on gfx950
+// (MI355X), and the prefill launcher, which sends bf16 inputs to the kernel in
+// gdn_prefill_bf16.hip.
 //
 // Defined by: "[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
 // section "Why" (fresh prefill rows go through a 64-token chunk prefill);
@@ -17,16 +19,15 @@
 //     O   = scale (diag(gamma) Q S0 + (Q K^T o D o lower-incl-diagonal) U)
 //     S1  = gamma_last S0 + K^T (diag(e^(G_last - G)) U)
 //
-// One kernel.  A workgroup owns one sequence and HG value heads that share a key
-// head (HG = 2 for bf16 inputs when the GQA group size is even, else 1) and walks
-// the sequence's chunks in order.  Per value head, d_v is split into 32-column
+// One kernel.  A workgroup owns one sequence and one value head and walks the
+// sequence's chunks in order.  Per value head, d_v is split into 32-column
 // strips, one wave each; a wave keeps its strip of S (d_k x 32, fp32) in MFMA
 // accumulator registers for the whole sequence.  The d_v columns of S, U and O are
 // independent, so strips never exchange data.  Per chunk:
-//   load     Q and K rows (shared by the HG heads) from the registers they were
+//   load     Q and K rows from the registers they were
 //            prefetched into during the previous chunk; V fragments likewise
-//   phase 1  gates by a wave scan; K K^T and Q K^T (lower tiles, shared by the HG
-//            heads) and Z = K S for each strip, on MFMA
+//   phase 1  gates by a wave scan; K K^T and Q K^T (lower tiles) and Z = K S for
+//            each strip, on MFMA
 //   phase 2  A for each head into LDS (fp32)
 //   phase 3  T = (I + A)^-1 in place, one wave per head: the 16x16 diagonal blocks by
 //            forward substitution (lane 16b + j owns column j of block b), then
@@ -35,12 +36,8 @@
 //   phase 4  T1 and -T2, split once per chunk into LDS (all threads)
 //   phase 5  P into LDS; U = T1 V + (-T2) Z; O = gamma o (Q S) + P U; the state
 //            update; the grid export
-// Precision.  For bf16 inputs the MFMAs are 16x16x32 bf16.  q, k and v are exact in
-// bf16; the derived operands that carry most of the rounding error -- T1, T2 and
-// the decayed U -- enter as a hi + lo pair of bf16 values (x = hi + lo to about
-// 2^-17), two MFMAs against the other operand.  Z, P and S enter as single bf16
-// values.  For fp32 inputs the MFMAs are 16x16x4 fp32 and nothing is split.
-// States, accumulators, gates and T's solve are fp32.  A sequence's work never
+// Precision.  The MFMAs are 16x16x4 fp32 and nothing is rounded below fp32: states,
+// accumulators, gates and T's solve are fp32.  A sequence's work never
 // depends on the other sequences of the call, so its results are bitwise
 // independent of its batch-mates; the chunks lie on the absolute 64-token grid, so
 // a resume from an exported grid state continues with the same arithmetic.
@@ -55,123 +52,20 @@ namespace {
 constexpr int kC = 64;   // chunk length
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- MFMA traits
 //
 // 16x16 output tiles.  Lane l holds A[l % 16][k...] and B[k...][l % 16]; the C/D tile
 // is held as C[4 (l / 16) + i][l % 16], i = 0..3.  Which k a lane element stands for
-// only has to agree between A and B, so two k orders are used:
-//   natural   element e of lane group g is k = KSTEP*ks + (bf16: 8g + e; fp32: g)
+// only has to agree between A and B, so two k orders are used (16x16x4 fp32, one
+// element per lane and step):
+//   natural   lane group g holds k = 4 ks + g
 //   from-C    the order in which a C tile's registers already sit, so that an fp32
 //             accumulator tile can feed the next MFMA as its B operand without an
-//             LDS round trip: bf16 step ks covers rows 32ks..32ks+31 with element e<4
-//             = row 32ks + 4g + e and e>=4 = row 32ks + 16 + 4g + (e-4); fp32 step
-//             ks is register (ks & 3) of C tile (ks >> 2), i.e. row 16(ks>>2) + 4g + (ks&3).
+//             LDS round trip: step ks is register (ks & 3) of C tile (ks >> 2), i.e.
+//             row 16 (ks >> 2) + 4 g + (ks & 3).
 template <typename E>
 struct Mma;
-
-template <>
-struct Mma<__bf16> {
-    static constexpr int KSTEP = 32;
-    typedef bf16x8 frag;
-    struct pair { frag hi, lo; };
-
-    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    // A split, B exact: hi then lo
-    static __device__ __forceinline__ f32x4 mma_sa(const pair& a, frag b, f32x4 c) {
-        c = mma(a.hi, b, c);
-        return mma(a.lo, b, c);
-    }
-    // A exact, B split: hi then lo
-    static __device__ __forceinline__ f32x4 mma_sb(frag a, const pair& b, f32x4 c) {
-        c = mma(a, b.hi, c);
-        return mma(a, b.lo, c);
-    }
-    static __device__ __forceinline__ int nat(int ks, int g, int e) { return 32 * ks + 8 * g + e; }
-    static __device__ __forceinline__ int fromc(int ks, int g, int e) {
-        return 32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-    }
-    static __device__ __forceinline__ pair split(const float* x) {
-        pair p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const __bf16 h = (__bf16)x[e];
-            p.hi[e] = h;
-            p.lo[e] = (__bf16)(x[e] - (float)h);   // exact difference, rounded once
-        }
-        return p;
-    }
-    static __device__ __forceinline__ frag round(const float* x) {
-        frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (__bf16)x[e];
-        return f;
-    }
-    // natural fragment from a row-major LDS row
-    static __device__ __forceinline__ frag row_nat(const __bf16* row, int ks, int g) {
-        return *reinterpret_cast<const bf16x8*>(row + 32 * ks + 8 * g);
-    }
-    // from-C ordered fragment from a row-major LDS row
-    static __device__ __forceinline__ frag row_fromc(const __bf16* row, int ks, int g) {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * ks + 4 * g);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * ks + 16 + 4 * g);
-        frag f;
-        f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-        f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-        return f;
-    }
-    // natural fragment down a column of a row-major LDS matrix
-    static __device__ __forceinline__ frag col_nat(const __bf16* m, int ld, int col, int ks, int g) {
-        frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = m[nat(ks, g, e) * ld + col];
-        return f;
-    }
-    // from-C ordered fragment down a column
-    static __device__ __forceinline__ frag col_fromc(const __bf16* m, int ld, int col, int ks, int g) {
-        frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = m[fromc(ks, g, e) * ld + col];
-        return f;
-    }
-    // natural fragment of an fp32 LDS row scaled per k, split into hi + lo
-    static __device__ __forceinline__ pair row_nat_scaled_split(const float* row, int ks, int g,
-                                                                const float* scale) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = row[nat(ks, g, e)] * scale[nat(ks, g, e)];
-        return split(x);
-    }
-    // B fragment (from-C order, step ks) out of 16-row accumulator tiles tiles[x * stride]
-    static __device__ __forceinline__ frag acc_fromc(const f32x4* tiles, int ks, int stride) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = tiles[(2 * ks) * stride][i];
-            x[4 + i] = tiles[(2 * ks + 1) * stride][i];
-        }
-        return round(x);
-    }
-    // the same, each row r scaled by scale[r] (or not, when scale is null), split
-    static __device__ __forceinline__ pair acc_fromc_split(const f32x4* tiles, int ks, int stride, int g,
-                                                           const float* scale) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = tiles[(2 * ks) * stride][i];
-            x[4 + i] = tiles[(2 * ks + 1) * stride][i];
-            if (scale) {
-                x[i] *= scale[32 * ks + 4 * g + i];
-                x[4 + i] *= scale[32 * ks + 16 + 4 * g + i];
-            }
-        }
-        return split(x);
-    }
-};
 
 template <>
 struct Mma<float> {
@@ -211,8 +105,6 @@ struct Mma<float> {
 
 template <typename E>
 struct Pad;   // LDS row padding in elements (keeps 16-byte row alignment, spreads banks)
-template <>
-struct Pad<__bf16> { static constexpr int value = 8; };
 template <>
 struct Pad<float> { static constexpr int value = 4; };
 
@@ -285,15 +177,9 @@ struct ScanSmem {
     } hd[HG];
 };
 
-// split an fp32 value into the operand type: hi (+ lo for bf16)
+// store an fp32 value as the operand type (fp32: as it is; the lo part is unused)
 template <typename E>
 __device__ __forceinline__ void split_store(E* hi, E* lo, int idx, float x);
-template <>
-__device__ __forceinline__ void split_store<__bf16>(__bf16* hi, __bf16* lo, int idx, float x) {
-    const __bf16 h = (__bf16)x;
-    hi[idx] = h;
-    lo[idx] = (__bf16)(x - (float)h);
-}
 template <>
 __device__ __forceinline__ void split_store<float>(float* hi, float*, int idx, float x) {
     hi[idx] = x;
@@ -789,12 +675,6 @@ hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int, int, int, int64_t) { return 0; }
-
-int prefill_heads_per_group(int dtype, int H_k, int H_v) {
-    // Two value heads that share a key head go to one workgroup (bf16 only: the fp32
-    // operand buffers of two heads do not fit in LDS).
-    return (dtype == 1 && (H_v / H_k) % 2 == 0) ? 2 : 1;
-}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;

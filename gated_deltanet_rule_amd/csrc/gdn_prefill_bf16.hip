@@ -173,7 +173,9 @@ struct Smem {
     static constexpr int BLD = 24;            // rows of a 16x16 bf16 block (12 dwords:
                                               // a half wave's 8-byte row reads are
                                               // bank-conflict free)
-    static constexpr int BSZ = 16 * BLD;
+    // block stride: 8 bf16 of padding put the four diagonal blocks (slots 0, 2, 5, 9),
+    // whose columns the first wave writes in one instruction, in different banks
+    static constexpr int BSZ = 16 * BLD + 8;
     static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
     static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
     __bf16 q[kC * QLD];

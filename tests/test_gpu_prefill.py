@@ -50,10 +50,18 @@ def test_prefill_single_sequence_fp32():
 
 @pytest.mark.parametrize("dtype,dk,dv,hk,hv", [("bf16", 128, 128, 2, 4), ("f32", 64, 64, 1, 2),
                                                ("bf16", 64, 128, 1, 1), ("f32", 128, 64, 2, 2),
-                                               ("bf16", 64, 64, 3, 6)])
+                                               ("bf16", 64, 64, 3, 6),
+                                               # the remaining bf16 kernel shapes: two value
+                                               # heads per workgroup (even group size) or one
+                                               # (odd: 1 or 3 value heads per key head)
+                                               ("bf16", 128, 64, 2, 4), ("bf16", 128, 64, 1, 3),
+                                               ("bf16", 128, 128, 3, 3), ("bf16", 64, 64, 2, 2),
+                                               ("bf16", 64, 128, 2, 4)])
 def test_prefill_varlen_ragged(dtype, dk, dv, hk, hv):
     """Ragged lengths (1, 63, 64, 65, 130, 200, 0), initial states from slots,
-    start positions on and off the 64 grid, exports every 64 tokens."""
+    start positions on and off the 64 grid, exports every 64 tokens; every
+    instantiation of the bf16 kernel (d_k, d_v in {64, 128}, one or two value heads
+    per workgroup)."""
     lengths = [1, 63, 64, 65, 130, 200, 0]
     starts = [0, 64, 5, 1000, 128, 33, 7]
     w = W.make_workload("rag", seed=21, H_k=hk, H_v=hv, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths,

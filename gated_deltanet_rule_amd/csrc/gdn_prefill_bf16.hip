@@ -33,8 +33,8 @@
 //            entering the accumulators through an identity product
 //   stage    after the first barrier, the next chunk's prefetched Q, K and V rows
 //            go to LDS (K and the gates by chunk parity), the first wave of each
-//            head scans the next gates from its registers, and the chunk after
-//            that is fetched into registers
+//            head scans the next gates from its registers; the chunk after that
+//            is fetched into registers once phase 3's state update is issued
 //   phase 3  per strip: the block solve for U, each output row block as soon as
 //            its U blocks exist, then the state update (K^T read from the K rows
 //            by transposing LDS reads) and the grid export
@@ -374,7 +374,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         }
     };
     // Loads run a chunk ahead of their staging: right after phase 1 of chunk c,
-    // chunk c + 1's inputs are staged and chunk c + 2's are fetched.
+    // chunk c + 1's inputs are staged; chunk c + 2's are fetched at the end of chunk
+    // c's phase 3.
     if (nchunks > 0) {
         prefetch_qk(0, (unsigned)tid);
         prefetch_v(0, (unsigned)tid);
@@ -568,10 +569,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             stage_qk(c + 1, (unsigned)tid_l);
             stage_v((unsigned)tid_l);
         }
-        if (c + 2 < nchunks) {
-            prefetch_qk(c + 2, (unsigned)tid_l);
-            prefetch_v(c + 2, (unsigned)tid_l);
-        }
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
@@ -699,6 +696,13 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+
+        // Chunk c + 2's loads go out here, after the state update: issued together with
+        // the staging at the start of phase 3, their burst delayed the solve.
+        if (c + 2 < nchunks) {
+            prefetch_qk(c + 2, (unsigned)tid_l);
+            prefetch_v(c + 2, (unsigned)tid_l);
+        }
 
         // ---- export on the grid
         if (a.export_grid > 0) {

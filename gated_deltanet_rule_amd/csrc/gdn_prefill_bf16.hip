@@ -39,9 +39,10 @@
 //            its U blocks exist, then the state update (K^T read from the K rows
 //            by transposing LDS reads) and the grid export
 // Precision.  All products are bf16 MFMA with fp32 accumulation.  q, k and v enter
-// exactly; S, Z and P enter as single bf16 values; every operand the solve and the
-// state update depend on -- the -A_ij and T_ii blocks, the right-hand sides, U and
-// the decayed U -- enters as a hi + lo pair of bf16 values (x = hi + lo to about
+// exactly; S, Z and P enter as single bf16 values, and so does U in the output
+// product P U (O is rounded to bf16 anyway); every operand the solve and the state
+// update depend on -- the -A_ij and T_ii blocks, the right-hand sides, U and the
+// decayed U -- enters as a hi + lo pair of bf16 values (x = hi + lo to about
 // 2^-17) in three products (hi hi, hi lo, lo hi) or two when the other side is
 // exact.  Gates, the A_ii inverses and all accumulators are fp32.  A sequence's work
 // never depends on the other sequences of the call, so its results are bitwise
@@ -615,7 +616,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[i][nt] = U;
                 Us[i][nt] = split4(U);
             }
-            // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, blocks in pairs
+            // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, blocks in pairs.
+            // U enters this product as its hi part only: O is rounded to bf16 on the way
+            // out, and nothing else depends on this product.
             const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
@@ -626,9 +629,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const bf16x4 h1 = j1 <= i ? Us[j1][nt].hi : z4;
-                    const bf16x4 l1 = j1 <= i ? Us[j1][nt].lo : z4;
                     Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, h1), pa, Oacc[i][nt]);
-                    Oacc[i][nt] = mma32(cat8(Us[j0][nt].lo, l1), pa, Oacc[i][nt]);
                 }
             }
             // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap

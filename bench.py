@@ -41,11 +41,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
                     help="prefill sequences (of 16) the oracle runs for the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE "
+                         "run and a --pmc WRITE_SIZE run of this bench into profiles/hbm_traffic.json")
     return ap.parse_args()
 
 
@@ -72,6 +75,40 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+def ingest_counters(fetch_csv, write_csv, copy_mib=1024):
+    """HBM bytes per launch of each library kernel from two rocprofv3 counter runs.
+    Each counter (KiB per dispatch) is scaled by what it reads for the plain copies of
+    copy_mib MiB that the bench dispatches (a copy reads and writes copy_mib MiB), so the
+    figures are in bytes whatever unit or sampling the counter uses on this chip."""
+    import csv
+    out = {}
+    per = {}
+    for tag, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = list(csv.DictReader(open(path)))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = [c for c in copies if c > 0.5 * max(copies)]
+        factor = (copy_mib * 1024.0) / float(np.median(big))
+        for kernel in KERNEL_SOURCES:
+            vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+            if vals:
+                per.setdefault(kernel, {})[tag] = (len(vals), float(np.mean(vals)), factor)
+    for kernel, d in per.items():
+        if "fetch" not in d or "write" not in d:
+            continue
+        nf, fk, ff = d["fetch"]
+        nw, wk, wf = d["write"]
+        out[kernel] = {"source": "gated_deltanet_rule_amd/csrc/" + KERNEL_SOURCES[kernel],
+                       "source_sha256": source_digest(kernel), "dispatches": [nf, nw],
+                       "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                       "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                       "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def algorithmic_flops_per_token(H_k, H_v, d_k, d_v, C=CHUNK):
     """Flops per prefill token of the chunked form, triangles counted once, K K^T and
     Q K^T once per key head: H_k 2 C d_k + H_v (C (d_k + d_v) + C d_v + 6 d_k d_v)."""
@@ -86,6 +123,9 @@ def algorithmic_bytes_per_token(H_k, H_v, d_k, d_v, elem):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

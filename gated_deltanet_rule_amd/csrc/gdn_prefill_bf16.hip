@@ -30,8 +30,10 @@
 //            K K^T and Q K^T (the HG heads share k and q) and turn them into the
 //            -A_ij blocks and the P blocks (scale folded in) of every head.  Then,
 //            per strip, Z = K S and Q S on MFMA and R = beta (V - gamma Z), V
-//            entering the accumulators through an identity product
-//   stage    after the first barrier, the next chunk's prefetched Q, K and V rows
+//            entering the accumulators through an identity product from the
+//            wave's own registers (each wave loads its V strip straight from HBM
+//            in that operand layout, a chunk ahead)
+//   stage    after the first barrier, the next chunk's prefetched Q and K rows
 //            go to LDS (K and the gates by chunk parity), the first wave of each
 //            head scans the next gates from its registers; the chunk after that
 //            is fetched into registers once phase 3's state update is issued
@@ -39,13 +41,12 @@
 //            its U blocks exist, then the state update (K^T read from the K rows
 //            by transposing LDS reads) and the grid export
 // Precision.  All products are bf16 MFMA with fp32 accumulation.  q, k and v enter
-// exactly; S, Z and P enter as single bf16 values, and so does U in the output
-// product P U (O is rounded to bf16 anyway); every operand the solve and the state
-// update depend on -- the -A_ij and T_ii blocks, the right-hand sides, U and the
-// decayed U -- enters as a hi + lo pair of bf16 values (x = hi + lo to about
-// 2^-17) in three products (hi hi, hi lo, lo hi) or two when the other side is
-// exact.  Gates, the A_ii inverses and all accumulators are fp32.  A sequence's work
-// never depends on the other sequences of the call, so its results are bitwise
+// exactly; S and Z enter as single bf16 values; every other operand -- the -A_ij,
+// T_ii and P blocks, the right-hand sides, U and the decayed U -- enters as a hi +
+// lo pair of bf16 values (x = hi + lo to about 2^-17) in three products (hi hi,
+// hi lo, lo hi) or two when the other side is exact.  Gates, the A_ii inverses and
+// all accumulators are fp32.  A sequence's work never depends on the other
+// sequences of the call, so its results are bitwise
 // independent of its batch-mates; chunks lie on the absolute 64-token grid, so a
 // resume from an exported grid state continues with the same arithmetic.
 #include <hip/hip_runtime.h>
@@ -170,7 +171,6 @@ struct Smem {
     // (8 rows x 32 bytes per half wave) and the staging writes all hit distinct
     // banks.
     static constexpr int QLD = DK + 16;
-    static constexpr int VLD = DV + 8;        // V rows (bf16)
     static constexpr int BLD = 24;            // rows of a 16x16 bf16 block (12 dwords:
                                               // a half wave's 8-byte row reads are
                                               // bank-conflict free)
@@ -183,9 +183,8 @@ struct Smem {
     __bf16 k[2][kC * QLD];                    // by chunk parity (the state update of chunk
                                               // c reads it while chunk c+1 is staged)
     struct Head {
-        __bf16 v[kC * VLD];
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
-        __bf16 p[10][BSZ];                    // P blocks
+        __bf16 p[10][2][BSZ];                 // P blocks; hi, lo
         float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
         float gate[2][kGates * kC];           // by chunk parity
     } hd[HG];
@@ -207,11 +206,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     constexpr int KS_DK = DK / 32;           // 32-wide k steps over d_k
     constexpr int VPR = DK / 8;              // 16-byte vectors per Q/K row
     constexpr int NQ = kC * VPR / NT;        // prefetched Q (and K) vectors per thread
-    constexpr int VPRV = DV / 8;             // 16-byte vectors per V row
-    constexpr int NPV = HG * kC * VPRV / NT; // prefetched V vectors per thread
     constexpr int NNL = HG * (NWH - 1);      // waves that are not the first of their head
     static_assert(NQ * NT == kC * VPR, "Q/K prefetch must divide evenly");
-    static_assert(NPV * NT == HG * kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
 
     const int G = a.H_v / a.H_k;
@@ -285,7 +281,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
     // ---- prefetch registers: Q/K row vectors, V row vectors, and (first wave of each
     //      head) this head's g and beta, one token per lane
     uint4 pq[NQ], pk[NQ];
-    uint4 pv[NPV];
+    // this wave's V strip of a chunk in the A-operand layout of the 16x16x16 identity
+    // product: pv[mt][nt] = V[16 mt + li][col0 + 16 nt + 4 g4 .. + 3]
+    bf16x4 pv[4][2];
     float gpf = 0.f, bpf = 0.f;
     auto ld16 = [](const void* base, uint32_t off) {
         return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
@@ -315,20 +313,22 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             bpf = (int)s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
         }
     };
-    // chunk c's V rows of the HG heads
-    auto prefetch_v = [&](int c, unsigned t) {
+    // chunk c's V strip of this wave, straight into registers (8 bytes per lane and
+    // tile: 16 rows x 32 bytes per instruction)
+    auto prefetch_v = [&](int c, int ln) {
         int b0, e0;
         dev::chunk_span(c, off64, len, b0, e0);
         const int tok = lo + b0, L = e0 - b0;
-        const __bf16* vb = vg + ((size_t)tok * a.H_v + h0) * DV;
+        const char* vb = reinterpret_cast<const char*>(vg + ((size_t)tok * a.H_v + h) * DV + col0);
+        const unsigned li = (unsigned)ln & 15u, g4 = (unsigned)ln >> 4;
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned hx = i / (kC * VPRV);
-            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
-            const uint32_t off = ((r * (unsigned)a.H_v + hx) * DV + vi * 8) * 2u;
-            pv[j] = (int)r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const unsigned r = 16u * mt + li;
+                const uint32_t off = (r * (unsigned)a.H_v * DV + 16u * nt + 4u * g4) * 2u;
+                pv[mt][nt] = (int)r < L ? *reinterpret_cast<const bf16x4*>(vb + off) : bf16x4{};
+            }
     };
     // Write chunk c's prefetched Q and K rows and the gates (those two by chunk parity)
     // to LDS.  For chunk c + 1 this runs right after the barrier that ends phase 1 of
@@ -363,29 +363,14 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             gt[GATE_TE * kC + ln] = __builtin_amdgcn_exp2f(G2_be - G2);
         }
     };
-    // Chunk c's V rows to LDS (for chunk c + 1 right after phase 1 of chunk c, the
-    // last reader of V).
-    auto stage_v = [&](unsigned t) {
-#pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned hx = i / (kC * VPRV);
-            const unsigned r = (i / VPRV) % kC, vi = i % VPRV;
-            *reinterpret_cast<uint4*>(sm.hd[hx].v + r * SM::VLD + vi * 8) = pv[j];
-        }
-    };
-    // Loads run a chunk ahead of their staging: right after phase 1 of chunk c,
-    // chunk c + 1's inputs are staged; chunk c + 2's are fetched at the end of chunk
-    // c's phase 3.
+    // Q and K loads run a chunk ahead of their staging: right after phase 1 of chunk
+    // c, chunk c + 1's Q and K rows are staged; chunk c + 2's are fetched at the end of
+    // chunk c's phase 3, after chunk c + 1's V strip (used in phase 1 of chunk c + 1).
     if (nchunks > 0) {
         prefetch_qk(0, (unsigned)tid);
-        prefetch_v(0, (unsigned)tid);
         stage_qk(0, (unsigned)tid);
-        stage_v((unsigned)tid);
-        if (nchunks > 1) {
-            prefetch_qk(1, (unsigned)tid);
-            prefetch_v(1, (unsigned)tid);
-        }
+        prefetch_v(0, lane);
+        if (nchunks > 1) prefetch_qk(1, (unsigned)tid);
     }
 
     for (int c = 0; c < nchunks; ++c) {
@@ -504,17 +489,20 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                             st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
                             st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
                         } else {
-                            st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4,
-                                __builtin_convertvector(acc * te * (a.scale * fr), bf16x4));
+                            const Split4 sp = split4(acc * te * (a.scale * fr));
+                            st4(hx.p[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                            st4(hx.p[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
                         }
                     } else {                     // a diagonal block of Q K^T: s <= r only
                         const float G2r = gx[GATE_G2 * kC + r];
                         const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
-                        bf16x4 pv4;
+                        f32x4 pd;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            pv4[e] = (__bf16)(s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f);
-                        st4(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, pv4);
+                            pd[e] = s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f;
+                        const Split4 sp = split4(pd);
+                        st4(hx.p[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                        st4(hx.p[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
                     }
                 }
             }
@@ -560,16 +548,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             for (int nt = 0; nt < 2; ++nt) {
                 Oacc[mt][nt] *= sg;
                 // + V through V I, onto -gamma Z
-                const bf16x4 av = ld4(hd.v + (16 * mt + li) * SM::VLD + col0 + 16 * nt + 4 * g4);
-                Racc[mt][nt] = mma16(av, ident, -gam * Racc[mt][nt]);
+                Racc[mt][nt] = mma16(pv[mt][nt], ident, -gam * Racc[mt][nt]);
                 Racc[mt][nt] *= bet;
             }
         }
         dev::lds_barrier();   // every -A_ij, T_ii and P block is complete
-        if (c + 1 < nchunks) {
-            stage_qk(c + 1, (unsigned)tid_l);
-            stage_v((unsigned)tid_l);
-        }
+        if (c + 1 < nchunks) stage_qk(c + 1, (unsigned)tid_l);
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
@@ -617,19 +601,24 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Us[i][nt] = split4(U);
             }
             // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, blocks in pairs.
-            // U enters this product as its hi part only: O is rounded to bf16 on the way
-            // out, and nothing else depends on this product.
+            // U and P both enter as hi + lo pairs (three products): when keys are highly
+            // correlated and gates near zero, U grows large and O is a small difference of
+            // large terms, where a single bf16 rounding of either side is too coarse.
             const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
                 const int j0 = 2 * kk, j1 = 2 * kk + 1;
-                const bf16x4 p0 = ld4(hd.p[blk(i, j0)] + li * SM::BLD + 4 * g4);
-                const bf16x4 p1 = j1 <= i ? ld4(hd.p[blk(i, j1)] + li * SM::BLD + 4 * g4) : z4;
-                const bf16x8 pa = cat8(p0, p1);
+                const bf16x8 ph = cat8(ld4(hd.p[blk(i, j0)][0] + li * SM::BLD + 4 * g4),
+                                       j1 <= i ? ld4(hd.p[blk(i, j1)][0] + li * SM::BLD + 4 * g4) : z4);
+                const bf16x8 pl = cat8(ld4(hd.p[blk(i, j0)][1] + li * SM::BLD + 4 * g4),
+                                       j1 <= i ? ld4(hd.p[blk(i, j1)][1] + li * SM::BLD + 4 * g4) : z4);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const bf16x4 h1 = j1 <= i ? Us[j1][nt].hi : z4;
-                    Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, h1), pa, Oacc[i][nt]);
+                    const bf16x8 uh = cat8(Us[j0][nt].hi, j1 <= i ? Us[j1][nt].hi : z4);
+                    const bf16x8 ul = cat8(Us[j0][nt].lo, j1 <= i ? Us[j1][nt].lo : z4);
+                    Oacc[i][nt] = mma32(uh, ph, Oacc[i][nt]);
+                    Oacc[i][nt] = mma32(ul, ph, Oacc[i][nt]);
+                    Oacc[i][nt] = mma32(uh, pl, Oacc[i][nt]);
                 }
             }
             // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap
@@ -700,10 +689,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 
         // Chunk c + 2's loads go out here, after the state update: issued together with
         // the staging at the start of phase 3, their burst delayed the solve.
-        if (c + 2 < nchunks) {
-            prefetch_qk(c + 2, (unsigned)tid_l);
-            prefetch_v(c + 2, (unsigned)tid_l);
-        }
+        if (c + 1 < nchunks) prefetch_v(c + 1, lane);
+        if (c + 2 < nchunks) prefetch_qk(c + 2, (unsigned)tid_l);
 
         // ---- export on the grid
         if (a.export_grid > 0) {

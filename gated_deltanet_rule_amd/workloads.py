@@ -106,9 +106,17 @@ def make_workload(name: str, *, seed: int, H_k: int, H_v: int, d_k: int, d_v: in
                   prefill_init: str = "zero", export_grid: int = 0,
                   start_pos: Optional[Sequence[int]] = None, scale: Optional[float] = None,
                   lengths_range: Optional[tuple] = None, num_seqs: Optional[int] = None,
-                  fill_pool: bool = True) -> Workload:
+                  fill_pool: bool = True, key_mix: float = 0.0, gate_scale: float = 1.0,
+                  beta_shift: float = 0.0) -> Workload:
     """Draw one workload.  ``lengths_range=(lo, hi)`` draws ``num_seqs`` integer
-    lengths uniformly in [lo, hi] (both ends inclusive) before anything else."""
+    lengths uniformly in [lo, hi] (both ends inclusive) before anything else.
+
+    Stress knobs (defaults leave the standard recipe untouched): ``key_mix = a > 0``
+    adds ``a sqrt(d_k)`` times one random unit direction per key head to every raw key
+    before normalisation, so that two keys of a head have a cosine near a^2 / (a^2 + 1)
+    (0.9 at a = 3); ``gate_scale`` multiplies g (near 0: almost no decay); ``beta_shift``
+    is added to beta's normal draw before the sigmoid (2: beta near 0.9).  The extra
+    direction is drawn after everything else, so the other draws do not move."""
     assert dtype in ("bf16", "f32")
     rng = np.random.default_rng(seed)
     if lengths_range is not None:
@@ -132,15 +140,21 @@ def make_workload(name: str, *, seed: int, H_k: int, H_v: int, d_k: int, d_v: in
 
     cast = round_to_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
     q = cast(_l2_normalise(rng.standard_normal((T, H_k, d_k), dtype=np.float32)))
-    k = cast(_l2_normalise(rng.standard_normal((T, H_k, d_k), dtype=np.float32)))
+    k_raw = rng.standard_normal((T, H_k, d_k), dtype=np.float32)
     v = cast(rng.standard_normal((T, H_v, d_v), dtype=np.float32))
     g = -_softplus(rng.standard_normal((T, H_v), dtype=np.float32))
-    beta = _sigmoid(rng.standard_normal((T, H_v), dtype=np.float32))
+    beta = _sigmoid(rng.standard_normal((T, H_v), dtype=np.float32) + np.float32(beta_shift))
+    if gate_scale != 1.0:
+        g = (g * np.float32(gate_scale)).astype(np.float32)
     if fill_pool:
         pool = rng.standard_normal((num_slots, H_v, d_k, d_v), dtype=np.float32)
         pool *= np.float32(state_std)
     else:
         pool = np.zeros((num_slots, H_v, d_k, d_v), dtype=np.float32)
+    if key_mix > 0.0:
+        u = _l2_normalise(rng.standard_normal((H_k, d_k), dtype=np.float32))
+        k_raw += np.float32(key_mix * math.sqrt(d_k)) * u[None]
+    k = cast(_l2_normalise(k_raw))
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
     sp = None if start_pos is None else np.asarray(start_pos, dtype=np.int32)

@@ -552,6 +552,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 Racc[mt][nt] *= bet;
             }
         }
+        // chunk c + 1's V strip: this chunk's was last read just above, and issued
+        // here its loads have all of phase 3 to land
+        if (c + 1 < nchunks) prefetch_v(c + 1, lane);
         dev::lds_barrier();   // every -A_ij, T_ii and P block is complete
         if (c + 1 < nchunks) stage_qk(c + 1, (unsigned)tid_l);
 
@@ -604,21 +607,34 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             // U and P both enter as hi + lo pairs (three products): when keys are highly
             // correlated and gates near zero, U grows large and O is a small difference of
             // large terms, where a single bf16 rounding of either side is too coarse.
+            // A block pair takes three 16x16x32 products; a last single block (even i)
+            // takes two, hi and lo of U side by side against P's hi twice, then U's hi
+            // against P's lo.
             const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
                 const int j0 = 2 * kk, j1 = 2 * kk + 1;
-                const bf16x8 ph = cat8(ld4(hd.p[blk(i, j0)][0] + li * SM::BLD + 4 * g4),
-                                       j1 <= i ? ld4(hd.p[blk(i, j1)][0] + li * SM::BLD + 4 * g4) : z4);
-                const bf16x8 pl = cat8(ld4(hd.p[blk(i, j0)][1] + li * SM::BLD + 4 * g4),
-                                       j1 <= i ? ld4(hd.p[blk(i, j1)][1] + li * SM::BLD + 4 * g4) : z4);
+                const bf16x4 ph0 = ld4(hd.p[blk(i, j0)][0] + li * SM::BLD + 4 * g4);
+                const bf16x4 pl0 = ld4(hd.p[blk(i, j0)][1] + li * SM::BLD + 4 * g4);
+                if (j1 <= i) {
+                    const bf16x8 ph = cat8(ph0, ld4(hd.p[blk(i, j1)][0] + li * SM::BLD + 4 * g4));
+                    const bf16x8 pl = cat8(pl0, ld4(hd.p[blk(i, j1)][1] + li * SM::BLD + 4 * g4));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const bf16x8 uh = cat8(Us[j0][nt].hi, j1 <= i ? Us[j1][nt].hi : z4);
-                    const bf16x8 ul = cat8(Us[j0][nt].lo, j1 <= i ? Us[j1][nt].lo : z4);
-                    Oacc[i][nt] = mma32(uh, ph, Oacc[i][nt]);
-                    Oacc[i][nt] = mma32(ul, ph, Oacc[i][nt]);
-                    Oacc[i][nt] = mma32(uh, pl, Oacc[i][nt]);
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const bf16x8 uh = cat8(Us[j0][nt].hi, Us[j1][nt].hi);
+                        const bf16x8 ul = cat8(Us[j0][nt].lo, Us[j1][nt].lo);
+                        Oacc[i][nt] = mma32(uh, ph, Oacc[i][nt]);
+                        Oacc[i][nt] = mma32(ul, ph, Oacc[i][nt]);
+                        Oacc[i][nt] = mma32(uh, pl, Oacc[i][nt]);
+                    }
+                } else {
+                    const bf16x8 pp = cat8(ph0, ph0);
+                    const bf16x8 pl = cat8(pl0, z4);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, Us[j0][nt].lo), pp, Oacc[i][nt]);
+                        Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, z4), pl, Oacc[i][nt]);
+                    }
                 }
             }
             // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap
@@ -689,7 +705,6 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 
         // Chunk c + 2's loads go out here, after the state update: issued together with
         // the staging at the start of phase 3, their burst delayed the solve.
-        if (c + 1 < nchunks) prefetch_v(c + 1, lane);
         if (c + 2 < nchunks) prefetch_qk(c + 2, (unsigned)tid_l);
 
         // ---- export on the grid

@@ -1,0 +1,56 @@
+"""The bf16 prefill kernel's rounding scheme against the per-element bound, on the
+stress inputs of the GPU parity suite (keys with cosine near 0.9, gates near or at
+zero, beta near one), in the fp64 rounding model of tests/precision_model.py.
+
+It pins the design choice that P and U enter the output product as hi + lo pairs:
+with single bf16 values the model exceeds the bound on these inputs (as the kernel
+did on the GPU), with the pairs it stays well inside it.  The reference is the fp64
+oracle.  The bound is |x - ref| <= 2e-3 + 1e-2 |ref| for outputs and states."""
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_rule_amd import workloads as W
+from tests import precision_model as PM
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def _worst_ratio(split_output, d, key_mix, gate_scale, beta_shift, chains):
+    w = W.make_workload("stress", seed=28, H_k=2, H_v=4, d_k=d, d_v=d, dtype="bf16",
+                        lengths=[700, 64, 1, 333, 129], num_slots=24, prefill_init="slots",
+                        key_mix=key_mix, gate_scale=gate_scale, beta_shift=beta_shift)
+    cu = w.cu_seqlens()
+    ref_o, finals, _, _ = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, cu, scale=w.scale,
+                                         pool=w.pool.astype(np.float64), init_slot=w.init_slot,
+                                         final_slot=w.final_slot)
+    worst_o = worst_s = 0.0
+    for seq, h in chains:
+        a, b = int(cu[seq]), int(cu[seq + 1])
+        kh = h // (w.H_v // w.H_k)
+        f64 = lambda x: np.asarray(x, dtype=np.float64)
+        o, S = PM.chain(f64(w.q[a:b, kh]), f64(w.k[a:b, kh]), f64(w.v[a:b, h]), f64(w.g[a:b, h]),
+                        f64(w.beta[a:b, h]), w.scale, f64(w.pool[w.init_slot[seq], h]), split_output)
+        ro, rs = ref_o[a:b, h], finals[seq, h]
+        worst_o = max(worst_o, float(np.max(np.abs(o - ro) / (ATOL + RTOL * np.abs(ro)))))
+        worst_s = max(worst_s, float(np.max(np.abs(S - rs) / (ATOL + RTOL * np.abs(rs)))))
+    return worst_o, worst_s
+
+
+CASES = {
+    # (d, key_mix, gate_scale, beta_shift, chains): the chains the earlier form fails on
+    "no decay, d 128": (128, 3.0, 0.0, 3.0, [(0, 1), (0, 3), (3, 0)]),
+    "near-zero decay, d 64": (64, 3.0, 0.01, 2.0, [(1, 2), (0, 3), (3, 3)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_split_output_product_meets_the_bound(name):
+    o, s = _worst_ratio(True, *CASES[name])
+    assert o < 0.5 and s < 0.6, (name, o, s)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_single_bf16_output_product_exceeds_the_bound(name):
+    o, _ = _worst_ratio(False, *CASES[name])
+    assert o > 1.0, (name, o)

@@ -139,3 +139,30 @@ def test_mixed_step_with_exports_and_resume_from_cache():
             assert_close("final", d["pool"][int(w.final_slot[i]), h].cpu().numpy(), rf, atol, rtol)
             got = exp_states[offs[i]:offs[i + 1], h].cpu().numpy()
             assert_close("exports", got, rexp, atol, rtol)
+
+
+def test_mixed_step_on_a_side_stream():
+    """A call enqueues on the stream it is given: the mixed step issued on a side
+    stream (inputs made ready by an event, results read after the stream is synchronised)
+    equals the same step on the default stream bitwise."""
+    w = W.make_workload("side", seed=31, H_k=2, H_v=4, d_k=128, d_v=128, dtype="bf16", num_decode_rows=5,
+                        lengths=[130, 64, 7], num_slots=24, export_grid=64)
+    d = to_device(w)
+    pool0 = d["pool"].clone()
+    o_ref = torch.empty_like(d["v"])
+    exp_ref = _mixed(w, d, d["pool"], o_ref, export=True)
+    torch.cuda.synchronize()
+    pool_ref = d["pool"].clone()
+
+    d["pool"].copy_(pool0)
+    o_side = torch.full_like(d["v"], float("nan"))
+    ready = torch.cuda.Event()
+    ready.record()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        side.wait_event(ready)
+        exp_side = _mixed(w, d, d["pool"], o_side, export=True)
+    side.synchronize()
+    assert torch.equal(o_side, o_ref)
+    assert torch.equal(d["pool"], pool_ref)
+    assert torch.equal(exp_side, exp_ref)

@@ -567,8 +567,9 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 // blocks j in pairs on 16x16x32 (the pair's U registers side by side are
-                // the from-C operand), a last odd block on 16x16x32 too, with a zero
-                // second half.  Every product that accumulates into X has one shape:
+                // the from-C operand); a last odd block on 16x16x32 too, with A's hi and
+                // lo side by side against U's hi twice, then against U's lo twice (the
+                // lo lo term comes free).  Every product that accumulates into X has one shape:
                 // back-to-back dependent MFMAs pass the accumulator on without wait
                 // states only between identical instructions, and the compiler does not
                 // pad a 16x16x32 -> 16x16x16 switch on the same registers.
@@ -587,12 +588,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 }
                 if (i & 1) {
                     const int j = i - 1;
-                    const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-                    const bf16x8 ah = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4), z4);
-                    const bf16x8 al = cat8(ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4), z4);
-                    X = mma32(ah, cat8(Us[j][nt].hi, z4), X);
-                    X = mma32(ah, cat8(Us[j][nt].lo, z4), X);
-                    X = mma32(al, cat8(Us[j][nt].hi, z4), X);
+                    const bf16x8 a2 = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
+                                           ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4));
+                    X = mma32(a2, cat8(Us[j][nt].hi, Us[j][nt].hi), X);
+                    X = mma32(a2, cat8(Us[j][nt].lo, Us[j][nt].lo), X);
                 }
                 const Split4 xs = split4(X);
                 const bf16x4 th = ld4(hd.sol[blk(i, i)][0] + li * SM::BLD + 4 * g4);
@@ -608,9 +607,8 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             // correlated and gates near zero, U grows large and O is a small difference of
             // large terms, where a single bf16 rounding of either side is too coarse.
             // A block pair takes three 16x16x32 products; a last single block (even i)
-            // takes two, hi and lo of U side by side against P's hi twice, then U's hi
-            // against P's lo.
-            const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            // takes two, hi and lo of U side by side against P's hi twice, then against
+            // P's lo twice.
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
                 const int j0 = 2 * kk, j1 = 2 * kk + 1;
@@ -629,11 +627,12 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                     }
                 } else {
                     const bf16x8 pp = cat8(ph0, ph0);
-                    const bf16x8 pl = cat8(pl0, z4);
+                    const bf16x8 pl = cat8(pl0, pl0);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
-                        Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, Us[j0][nt].lo), pp, Oacc[i][nt]);
-                        Oacc[i][nt] = mma32(cat8(Us[j0][nt].hi, z4), pl, Oacc[i][nt]);
+                        const bf16x8 u2 = cat8(Us[j0][nt].hi, Us[j0][nt].lo);
+                        Oacc[i][nt] = mma32(u2, pp, Oacc[i][nt]);
+                        Oacc[i][nt] = mma32(u2, pl, Oacc[i][nt]);
                     }
                 }
             }

@@ -72,20 +72,26 @@ def test_prefill_varlen_ragged(dtype, dk, dv, hk, hv):
     _check(w, d, exp_states, prefill_reference(w))
 
 
-@pytest.mark.parametrize("dtype,dk,dv,key_mix,gate_scale,beta_shift", [
-    ("bf16", 128, 128, 3.0, 0.01, 2.0),      # keys with cosine near 0.9, almost no decay, beta near 0.85
-    ("bf16", 128, 128, 3.0, 0.0, 3.0),       # no decay at all, beta near 0.95
-    ("bf16", 64, 64, 3.0, 0.01, 2.0),
-    ("bf16", 128, 128, 1.0, 0.1, 0.0),       # cosine near 0.5, slow decay
-    ("f32", 128, 128, 3.0, 0.01, 2.0)])
-def test_prefill_stress_inputs(dtype, dk, dv, key_mix, gate_scale, beta_shift):
+@pytest.mark.parametrize("dtype,dk,dv,hk,hv,key_mix,gate_scale,beta_shift", [
+    ("bf16", 128, 128, 2, 4, 3.0, 0.01, 2.0),   # keys with cosine near 0.9, almost no decay, beta near 0.85
+    ("bf16", 128, 128, 2, 4, 3.0, 0.0, 3.0),    # no decay at all, beta near 0.95
+    ("bf16", 64, 64, 2, 4, 3.0, 0.01, 2.0),
+    ("bf16", 128, 128, 2, 4, 1.0, 0.1, 0.0),    # cosine near 0.5, slow decay
+    # the other bf16 kernel shapes: d_k != d_v, one value head per workgroup (odd group)
+    ("bf16", 128, 64, 2, 4, 3.0, 0.0, 3.0),
+    ("bf16", 64, 128, 2, 4, 3.0, 0.0, 3.0),
+    ("bf16", 128, 128, 1, 3, 3.0, 0.0, 3.0),
+    ("bf16", 64, 64, 1, 3, 3.0, 0.01, 2.0),
+    ("f32", 128, 128, 2, 4, 3.0, 0.01, 2.0),
+    ("f32", 64, 64, 2, 4, 3.0, 0.0, 3.0)])
+def test_prefill_stress_inputs(dtype, dk, dv, hk, hv, key_mix, gate_scale, beta_shift):
     """Inputs that make the in-chunk triangular system ill-conditioned: highly
     correlated keys (so K K^T is near rank one and I + A has large off-diagonal
     entries), gates near zero (nothing in D damps them) and beta near one.  The
     split-precision solve must still meet the same per-element bound as on the
     standard inputs, for outputs, final states and every export."""
     lengths = [700, 64, 1, 333, 129]
-    w = W.make_workload("stress", seed=28, H_k=2, H_v=4, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths,
+    w = W.make_workload("stress", seed=28, H_k=hk, H_v=hv, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths,
                         num_slots=24, prefill_init="slots", export_grid=64, key_mix=key_mix,
                         gate_scale=gate_scale, beta_shift=beta_shift)
     d = to_device(w)

@@ -139,8 +139,9 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows,
  *              state_pool[final_slot[i]] (skipped when outside the range).  It may
  *              equal the sequence's own init_slot (resume in place).
  *   start_pos  device [num_seqs] int32 or NULL (= all 0): absolute position of each
- *              sequence's first token.  Chunks lie on the absolute 64-token grid: a
- *              sequence starting off the grid begins with a short chunk.
+ *              sequence's first token, >= 0 (a negative value is outside the contract:
+ *              the device cannot be checked without a sync).  Chunks lie on the absolute
+ *              64-token grid: a sequence starting off the grid begins with a short chunk.
  *   export_grid 0 = no export.  Otherwise a positive multiple of 64 (for example 64,
  *              or 1088 = lcm(64, 1088)); the state after every absolute position p with
  *              p % export_grid == 0 and start_pos < p <= start_pos + length is written

@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
+    ap.add_argument("--ingest-sq-counters", metavar="SQ_CSV",
+                    help="no GPU work: turn the counter_collection.csv of a rocprofv3 --pmc run with "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_* and SQ_WAVES into "
+                         "profiles/mfma_counters.json")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE "
                          "run and a --pmc WRITE_SIZE run of this bench into profiles/hbm_traffic.json")
@@ -109,6 +113,62 @@ def ingest_counters(fetch_csv, write_csv, copy_mib=1024):
     print(json.dumps(out, indent=1))
 
 
+SIMDS = 1024          # 256 compute units x 4 SIMDs
+XCDS = 8
+
+
+def ingest_sq_counters(sq_csv, chunks_per_wave=128):
+    """MFMA utilisation of each library kernel from one rocprofv3 counter run: busy
+    cycles of the matrix cores summed over all SIMDs, over the GPU-active cycles (the
+    GRBM counter summed over the XCDs, divided by their number) times the SIMD count;
+    the instruction counts per wave (and per chunk for the prefill kernel, whose
+    waves each walk chunks_per_wave chunks at the bench's shape)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(sq_csv)):
+        kernel = next((k for k in KERNEL_SOURCES if k in r["Kernel_Name"]), None)
+        if kernel:
+            d = per.setdefault(kernel, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for kernel, disp in per.items():
+        mean = lambda c: float(np.mean([d[c] for d in disp.values()]))
+        active = mean("GRBM_GUI_ACTIVE") / XCDS
+        waves = mean("SQ_WAVES")
+        units = waves * (chunks_per_wave if kernel == "chunk_kernel" else 1)
+        rec = {"source": "gated_deltanet_rule_amd/csrc/" + KERNEL_SOURCES[kernel],
+               "source_sha256": source_digest(kernel), "dispatches": len(disp),
+               "mfma_busy_frac": round(mean("SQ_VALU_MFMA_BUSY_CYCLES") / (active * SIMDS), 4),
+               "gpu_active_cycles_per_xcd": round(active),
+               "mfma_insts_per_unit": round(mean("SQ_INSTS_MFMA") / units, 1),
+               "valu_insts_per_unit": round((mean("SQ_INSTS_VALU") - mean("SQ_INSTS_MFMA")) / units, 1),
+               "lds_insts_per_unit": round(mean("SQ_INSTS_LDS") / units, 1),
+               "unit": "wave and chunk" if kernel == "chunk_kernel" else "wave",
+               "executed_bf16_mfma_flop": mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512}
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in next(iter(disp.values())):
+            busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+            rec["valu_coexec_frac_of_mfma_busy"] = round(mean("SQ_VALU_MFMA_COEXEC_CYCLES") / busy, 4) if busy else None
+        out[kernel] = rec
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def measured_mfma_util(kernel):
+    """MFMA busy fraction from the committed counter profile, or None when there is
+    none for the current source of the kernel."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "mfma_counters.json")) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("mfma_busy_frac")
+
+
 def algorithmic_flops_per_token(H_k, H_v, d_k, d_v, C=CHUNK):
     """Flops per prefill token of the chunked form, triangles counted once, K K^T and
     Q K^T once per key head: H_k 2 C d_k + H_v (C (d_k + d_v) + C d_v + 6 d_k d_v)."""
@@ -125,6 +185,9 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_sq_counters:
+        ingest_sq_counters(args.ingest_sq_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -249,6 +312,7 @@ def main():
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                         "bytes_per_launch": pre_bytes, "traffic": measured_traffic("chunk_kernel"),
                         "mfma_tflops": round(pre_tflops, 2), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                        "mfma_busy_frac_counters": measured_mfma_util("chunk_kernel"),
                         "flops_per_launch": pre_flops},
     }
     dominant = "chunk_kernel" if t_pre >= t_dec else "decode_kernel"

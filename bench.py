@@ -290,6 +290,7 @@ def main():
     ms_step = total_ms / K
     t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     t_pre = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    t_dec_b2b = decode_back_to_back(torch, binding, wd, dq, dk_, dv_, dg, db, do, pool, dev)
 
     # ---- figures
     value = Tp / (ms_step * 1e-3)
@@ -330,7 +331,12 @@ def main():
                    "global_batch": B + N, "seq_len": 8192, "prefill_tokens": Tp, "decode_rows": B,
                    "parallelism": "single GPU"},
         "decode": {"state_GB_per_s": round(dec_gbps, 1), "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "ms": round(t_dec, 5), "state_bytes": dec_bytes},
+                   "ms": round(t_dec, 5), "state_bytes": dec_bytes,
+                   # the same launch timed back to back over 4 disjoint 64-slot sets of the
+                   # 256-slot cache (every launch's states cold), without a pair of events
+                   # around each launch
+                   "back_to_back_ms": round(t_dec_b2b, 5),
+                   "back_to_back_frac_of_hbm_peak": round(dec_bytes / (t_dec_b2b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": round(t_pre, 4),
                     "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                     "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok,
@@ -345,6 +351,28 @@ def main():
     print("input generation %.1f s; step %.3f ms = decode %.4f + prefill %.4f ms" % (
         gen_s, ms_step, t_dec, t_pre), file=sys.stderr)
     print(json.dumps(out), flush=True)
+
+
+def decode_back_to_back(torch, binding, wd, q, k, v, g, beta, o, pool, dev, rounds=5):
+    """Average duration of the decode launch over rounds x 4 launches issued back to
+    back, each on a different one of 4 disjoint 64-slot sets that cover the 256-slot
+    cache (in place), so that no launch finds its states in a cache.  Returns ms."""
+    B = wd.num_decode_rows
+    slots = wd.pool.shape[0]
+    nsets = slots // B
+    perm = np.concatenate([wd.slot_in, np.setdiff1d(np.arange(slots), wd.slot_in)]).astype(np.int32)
+    sets = [torch.as_tensor(perm[i * B:(i + 1) * B], device=dev) for i in range(nsets)]
+    for s in sets:
+        binding.gdn_recurrent_decode(q, k, v, g, beta, o, pool, s, s, scale=wd.scale)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(rounds):
+        for s in sets:
+            binding.gdn_recurrent_decode(q, k, v, g, beta, o, pool, s, s, scale=wd.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (rounds * nsets)
 
 
 def copy_bandwidth(torch, dev, mib=1024, reps=10):

@@ -14,7 +14,8 @@ is finer than the kernel's fp32 and does not change what the model is for: showi
 which roundings a bound can or cannot absorb.
 
 ``split_output=False`` models the earlier form in which P and U entered the output
-product as single bf16 values.
+product as single bf16 values; ``split_state_update=False`` drops the lo part of the
+decayed U in the state update.
 """
 from __future__ import annotations
 
@@ -44,7 +45,7 @@ def split_product(a, b):
     return ah @ bh + ah @ bl + al @ bh
 
 
-def chain(q, k, v, g, beta, scale, S0, split_output=True):
+def chain(q, k, v, g, beta, scale, S0, split_output=True, split_state_update=True):
     """One chain: q, k [T, d_k]; v [T, d_v]; g, beta [T]; S0 [d_k, d_v].  Returns
     (o [T, d_v] rounded to bf16, final state [d_k, d_v])."""
     T = q.shape[0]
@@ -76,5 +77,5 @@ def chain(q, k, v, g, beta, scale, S0, split_output=True):
         o[c0:c0 + L] = bf16(scale * gam[:, None] * (Q @ Sb) + PU)
         dU = np.exp(G[-1] - G)[:, None] * U
         hi, lo = split(dU)
-        S = gam[-1] * S + K.T @ hi + K.T @ lo
+        S = gam[-1] * S + K.T @ hi + (K.T @ lo if split_state_update else 0.0)
     return o, S

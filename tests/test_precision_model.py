@@ -16,7 +16,7 @@ from tests import precision_model as PM
 ATOL, RTOL = 2e-3, 1e-2
 
 
-def _worst_ratio(split_output, d, key_mix, gate_scale, beta_shift, chains):
+def _worst_ratio(split_output, d, key_mix, gate_scale, beta_shift, chains, split_state_update=True):
     w = W.make_workload("stress", seed=28, H_k=2, H_v=4, d_k=d, d_v=d, dtype="bf16",
                         lengths=[700, 64, 1, 333, 129], num_slots=24, prefill_init="slots",
                         key_mix=key_mix, gate_scale=gate_scale, beta_shift=beta_shift)
@@ -30,7 +30,8 @@ def _worst_ratio(split_output, d, key_mix, gate_scale, beta_shift, chains):
         kh = h // (w.H_v // w.H_k)
         f64 = lambda x: np.asarray(x, dtype=np.float64)
         o, S = PM.chain(f64(w.q[a:b, kh]), f64(w.k[a:b, kh]), f64(w.v[a:b, h]), f64(w.g[a:b, h]),
-                        f64(w.beta[a:b, h]), w.scale, f64(w.pool[w.init_slot[seq], h]), split_output)
+                        f64(w.beta[a:b, h]), w.scale, f64(w.pool[w.init_slot[seq], h]), split_output,
+                        split_state_update)
         ro, rs = ref_o[a:b, h], finals[seq, h]
         worst_o = max(worst_o, float(np.max(np.abs(o - ro) / (ATOL + RTOL * np.abs(ro)))))
         worst_s = max(worst_s, float(np.max(np.abs(S - rs) / (ATOL + RTOL * np.abs(rs)))))
@@ -54,3 +55,19 @@ def test_split_output_product_meets_the_bound(name):
 def test_single_bf16_output_product_exceeds_the_bound(name):
     o, _ = _worst_ratio(False, *CASES[name])
     assert o > 1.0, (name, o)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_state_update_without_lo_exceeds_the_bound(name):
+    """The decayed U enters the state update as a hi + lo pair: with its hi part only,
+    the states leave the bound on the stress inputs."""
+    _, s = _worst_ratio(True, *CASES[name], split_state_update=False)
+    assert s > 1.0, (name, s)
+
+
+def test_standard_inputs_are_well_inside_the_bound():
+    """The standard input recipe (independent unit keys, g = -softplus(N(0,1)), beta =
+    sigmoid(N(0,1))) with the kernel's roundings: outputs and states stay far inside
+    the bound."""
+    o, s = _worst_ratio(True, 128, 0.0, 1.0, 0.0, [(0, 0), (0, 3), (3, 1), (4, 2)])
+    assert o < 0.3 and s < 0.1, (o, s)

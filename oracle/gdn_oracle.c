@@ -32,6 +32,12 @@
  * Every loop below is the definition written out: no blocking, no reordering, no
  * chunking.  All arithmetic is in double precision; inputs arrive already widened
  * from the exact values the GPU receives.
+ *
+ * Parity unpinned: the output scale (a parameter), the GQA head map above and the
+ * [d_k][d_v] state layout are conventions the pages do not fix; the oracle and the
+ * GPU library share them by definition, and no pin can check them.  Everything
+ * else is pinned by the tests (brute-force products, exact rationals, closed forms,
+ * an independent chunked evaluation, planted mistakes).
  */
 #include <math.h>
 #include <stdint.h>

@@ -11,10 +11,18 @@ exactly what gdn_mixed_step enqueues (checked bitwise before timing), so that HI
 events on the launch stream time each kernel.  Inputs are resident in HBM before the
 timed region starts.
 
+Timing: W warm-up steps, then exactly K steps between one pair of HIP events
+(ms_per_step, value).  Per-kernel medians with 10th/90th percentiles come from a
+second pass of K steps with an event between the two launches; the prefill alone and
+the decode alone (over disjoint slot sets of the cache) are also timed back to back.
+
 Prints one JSON line: value = prefill tokens per second of the whole step; the
 decode part's state bandwidth and its fraction of the 8 TB/s HBM peak; the dominant
-kernel's roofline; and the fp64 CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+kernel's roofline; the other standard workloads (the single fp32 sequence, the
+varlen prefill exporting every 64 tokens, the mixed step of 32 cached rows and four
+fresh prefills), each timed call by call with the caches flushed in between; and
+the fp64 CPU oracle timed on bounded samples of the same workload, on every host
+core and on one.
 """
 import argparse
 import hashlib
@@ -31,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s + decode state GB/s (frac of HBM peak) on 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 CHUNK = 64
 KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "chunk_kernel": "gdn_prefill_bf16.hip"}
 
@@ -39,10 +48,12 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
-                    help="prefill sequences (of 16) the oracle runs for the CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the single-sequence, varlen and mixed-step workloads")
+    ap.add_argument("--secondary-calls", type=int, default=50,
+                    help="timed calls of each secondary workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
@@ -181,6 +192,132 @@ def algorithmic_bytes_per_token(H_k, H_v, d_k, d_v, elem):
     return 2 * H_k * d_k * elem + 2 * H_v * d_v * elem + 8 * H_v
 
 
+def stats(ts):
+    """Median, 10th and 90th percentile of a list of durations (ms)."""
+    a = np.sort(np.asarray(ts, dtype=np.float64))
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+def time_calls(torch, fn, n, warmup, flush=None):
+    """Durations (ms) of n calls of fn, each between a pair of HIP events recorded on
+    the stream the library launches on (torch's current stream); flush() runs before
+    every call, outside the events."""
+    for _ in range(warmup):
+        if flush:
+            flush()
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if flush:
+            flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def time_loop(torch, fn, n):
+    """Average duration (ms) of n calls of fn issued back to back between one pair of events."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def prefill_inputs(torch, binding, w, dev, B=0):
+    """A workload's tensors on the device, with an export buffer for its grid."""
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {x: torch.from_numpy(getattr(w, x)).to(dev, dt) for x in ("q", "k", "v")}
+    t.update({x: torch.from_numpy(getattr(w, x)).to(dev) for x in ("g", "beta", "pool")})
+    i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32), device=dev)
+    t["o"] = torch.empty_like(t["v"])
+    t["cu"] = i32(w.cu_seqlens())
+    t["init_slot"], t["final_slot"] = i32(w.init_slot), i32(w.final_slot)
+    t["slot_in"], t["slot_out"] = i32(w.slot_in), i32(w.slot_out)
+    kw = dict(scale=w.scale, workspace=binding.alloc_workspace(w.H_v, dt, w.num_seqs, w.prefill_tokens, dev))
+    if w.export_grid:
+        offs = binding.export_offsets(w.lengths, None, w.export_grid)
+        kw.update(export_grid=w.export_grid, export_offsets=i32(offs),
+                  export_states=torch.empty((max(offs[-1], 1), w.H_v, w.d_k, w.d_v), dtype=torch.float32,
+                                            device=dev))
+    n_states = (kw["export_states"].shape[0] if w.export_grid else 0) + w.num_seqs
+    return t, kw, n_states
+
+
+def prefill_figures(ms, w, n_states, elem):
+    """Throughput and roofline fractions of one prefill launch of ms milliseconds."""
+    T = w.prefill_tokens
+    bytes_ = algorithmic_bytes_per_token(w.H_k, w.H_v, w.d_k, w.d_v, elem) * T + 4 * w.H_v * w.d_k * w.d_v * n_states
+    flops = algorithmic_flops_per_token(w.H_k, w.H_v, w.d_k, w.d_v) * T
+    gbps = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak_t = BF16_PEAK_TFLOPS if elem == 2 else FP32_PEAK_TFLOPS
+    return {"tokens_per_s": round(T / (ms * 1e-3), 1), "bytes_per_launch": int(bytes_),
+            "flops_per_launch": int(flops), "achieved_GB_per_s": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "mfma_tflops": round(tflops, 3),
+            "mfma_frac": round(tflops / peak_t, 4),
+            # time a launch could take at best: its bytes at the HBM peak or its flops at
+            # the matrix peak, whichever is longer
+            "floor_ms": round(max(bytes_ / (HBM_PEAK_GBPS * 1e9), flops / (peak_t * 1e12)) * 1e3, 5)}
+
+
+def secondary_configs(torch, binding, W, dev, n, warmup):
+    """The other standard workloads, each timed call by call with the caches flushed
+    (a 1 GiB fill) before every call: the single fp32 sequence, the varlen prefill
+    with exports every 64 tokens, and the mixed step."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = lambda: scratch.fill_(1.0)
+    out = {}
+
+    w0 = W.config(0)
+    t, kw, ns = prefill_inputs(torch, binding, w0, dev)
+    run0 = lambda: binding.gdn_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["o"], t["cu"], t["pool"],
+                                             t["init_slot"], t["final_slot"], **kw)
+    st = stats(time_calls(torch, run0, n, warmup, flush))
+    out["single_sequence_fp32"] = dict(
+        {"workload": W.CONFIG_DESCRIPTIONS[0], "bound": "latency", "kernel": "scan_kernel", "ms": st},
+        **{k: v for k, v in prefill_figures(st["median"], w0, ns, 4).items()
+           if k in ("tokens_per_s", "flops_per_launch", "floor_ms")})
+    del t, kw
+
+    w2 = W.config(2, fill_pool=False)
+    t, kw, ns = prefill_inputs(torch, binding, w2, dev)
+    run2 = lambda: binding.gdn_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["o"], t["cu"], t["pool"],
+                                             t["init_slot"], t["final_slot"], **kw)
+    st = stats(time_calls(torch, run2, n, warmup, flush))
+    fig = prefill_figures(st["median"], w2, ns, 2)
+    out["varlen_prefill_export64"] = dict(
+        {"workload": W.CONFIG_DESCRIPTIONS[2], "lengths": w2.lengths, "prefill_tokens": w2.prefill_tokens,
+         "exported_states": ns - w2.num_seqs, "bound": "hbm", "kernel": "chunk_kernel", "ms": st}, **fig)
+    del t, kw
+
+    w3 = W.config(3)
+    t, kw, ns = prefill_inputs(torch, binding, w3, dev)
+    B = w3.num_decode_rows
+    run3 = lambda: binding.gdn_mixed_step(t["q"], t["k"], t["v"], t["g"], t["beta"], t["o"], t["pool"], t["slot_in"],
+                                          t["slot_out"], t["cu"], t["init_slot"], t["final_slot"], **kw)
+    st = stats(time_calls(torch, run3, n, warmup, flush))
+    dec_bytes = 2 * 4 * w3.d_k * w3.d_v * B * w3.H_v
+    pre = prefill_figures(st["median"], w3, ns, 2)
+    step_bytes = dec_bytes + pre["bytes_per_launch"]
+    out["mixed_step"] = {
+        "workload": W.CONFIG_DESCRIPTIONS[3], "bound": "latency", "kernels": ["decode_kernel", "chunk_kernel"],
+        "step_ms": st, "decode_rows": B, "prefill_tokens": w3.prefill_tokens,
+        "tokens_per_s": round((B + w3.prefill_tokens) / (st["median"] * 1e-3), 1),
+        "bytes_per_step": int(step_bytes),
+        "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBPS * 1e9) * 1e3, 5)}
+    del t, kw, scratch
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -255,13 +392,17 @@ def main():
     def stage_prefill():
         binding.gdn_chunk_prefill(pq, pk, pv, pg, pb, po, cu, pool, init_slot, final_slot, **pre)
 
+    def step():
+        stage_decode()
+        stage_prefill()
+
     # the staged step is the mixed step: check bitwise once, from the same pool
     pool0 = pool.clone()
     binding.gdn_mixed_step(q, k, v, g, beta, o, pool, slot_in, slot_out, cu, init_slot, final_slot, **pre)
     torch.cuda.synchronize()
     ref = (o.clone(), pool.clone(), exports.clone())
     pool.copy_(pool0)
-    stage_decode(); stage_prefill()
+    step()
     torch.cuda.synchronize()
     same = torch.equal(o, ref[0]) and torch.equal(pool, ref[1]) and torch.equal(exports, ref[2])
     if not same:
@@ -270,27 +411,30 @@ def main():
     del pool0, ref
 
     for _ in range(args.warmup):
-        stage_decode(); stage_prefill()
+        step()
     torch.cuda.synchronize()
 
+    # The timed region: exactly K steps between one pair of events, nothing else in it.
     K = args.steps
+    ms_step = time_loop(torch, step, K)
+
+    # Per-kernel figures from separate passes: K steps with an event between the two
+    # launches (median and spread per kernel), the prefill alone back to back, and the
+    # decode back to back over disjoint slot sets of the cache.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        ev[i][0].record()
+    for e in ev:
+        e[0].record()
         stage_decode()
-        ev[i][1].record()
+        e[1].record()
         stage_prefill()
-        ev[i][2].record()
-    end.record()
+        e[2].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K
-    t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    t_pre = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    st_dec = stats([e[0].elapsed_time(e[1]) for e in ev])
+    st_pre = stats([e[1].elapsed_time(e[2]) for e in ev])
+    t_pre_b2b = time_loop(torch, stage_prefill, K)
     t_dec_b2b = decode_back_to_back(torch, binding, wd, dq, dk_, dv_, dg, db, do, pool, dev)
+    t_dec, t_pre = st_dec["median"], st_pre["median"]
 
     # ---- figures
     value = Tp / (ms_step * 1e-3)
@@ -304,17 +448,17 @@ def main():
     pre_bytes = b_tok * Tp + state_bytes * (offs[-1] + N)  # activations + exports + final states
     pre_gbps = pre_bytes / (t_pre * 1e-3) / 1e9
     kernels = {
-        "decode_kernel": {"ms": round(t_dec, 5), "bound": "hbm", "achieved": round(dec_gbps, 1),
+        "decode_kernel": {"ms": st_dec, "bound": "hbm", "achieved": round(dec_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                           "bytes_per_launch": dec_bytes, "traffic": measured_traffic("decode_kernel")},
         # arithmetic intensity pre_flops / pre_bytes (about 156 flop/B) is below the bf16
         # ridge (2500 / 8 = 312 flop/B): HBM binds, MFMA use is reported beside it
-        "chunk_kernel": {"ms": round(t_pre, 4), "bound": "hbm", "achieved": round(pre_gbps, 1),
+        "chunk_kernel": {"ms": st_pre, "bound": "hbm", "achieved": round(pre_gbps, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                         "bytes_per_launch": pre_bytes, "traffic": measured_traffic("chunk_kernel"),
                         "mfma_tflops": round(pre_tflops, 2), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                         "mfma_busy_frac_counters": measured_mfma_util("chunk_kernel"),
-                        "flops_per_launch": pre_flops},
+                        "flops_per_launch": pre_flops, "back_to_back_ms": round(t_pre_b2b, 5)},
     }
     dominant = "chunk_kernel" if t_pre >= t_dec else "decode_kernel"
     roof = kernels[dominant]
@@ -331,13 +475,13 @@ def main():
                    "global_batch": B + N, "seq_len": 8192, "prefill_tokens": Tp, "decode_rows": B,
                    "parallelism": "single GPU"},
         "decode": {"state_GB_per_s": round(dec_gbps, 1), "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "ms": round(t_dec, 5), "state_bytes": dec_bytes,
+                   "ms": t_dec, "state_bytes": dec_bytes,
                    # the same launch timed back to back over 4 disjoint 64-slot sets of the
                    # 256-slot cache (every launch's states cold), without a pair of events
                    # around each launch
                    "back_to_back_ms": round(t_dec_b2b, 5),
                    "back_to_back_frac_of_hbm_peak": round(dec_bytes / (t_dec_b2b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": round(t_pre, 4),
+        "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": t_pre,
                     "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                     "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok,
                     "bytes_per_token": b_tok},
@@ -345,9 +489,11 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_secondary:
+        out["other_workloads"] = secondary_configs(torch, binding, W, dev, args.secondary_calls, args.warmup)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wp, wd, args.cpu_sample_seqs)
+        out["cpu_baseline"] = cpu_baseline(wp, wd)
     print("input generation %.1f s; step %.3f ms = decode %.4f + prefill %.4f ms" % (
         gen_s, ms_step, t_dec, t_pre), file=sys.stderr)
     print(json.dumps(out), flush=True)
@@ -394,30 +540,58 @@ def copy_bandwidth(torch, dev, mib=1024, reps=10):
     return gbps
 
 
-def cpu_baseline(wp, wd, n_seqs):
+def _median_runs(fn, runs=3, single_if_over_s=60.0):
+    """Median wall time (s) of up to `runs` calls of fn; one call when the first takes
+    longer than single_if_over_s."""
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+        if ts[0] > single_if_over_s:
+            break
+    return float(np.median(ts)), len(ts)
+
+
+def cpu_baseline(wp, wd, all_core_seqs=4, one_thread_tokens=2048):
     """The oracle as it stands (fp64 sequential recurrence, OpenMP over (sequence,
-    head) units) on a bounded sample of the same workload."""
+    head) units) on bounded samples of the same workloads: every host core on
+    all_core_seqs of the 16 long sequences (all 32 heads, exports on the 1088 grid),
+    and one thread on the first one_thread_tokens tokens of one sequence; each the
+    median of 3 runs (one run if a run exceeds 60 s).  Decode likewise on the whole
+    64-row batch."""
     import oracle
-    n_seqs = max(1, min(n_seqs, wp.num_seqs))
     L = wp.lengths[0]
+    n_seqs = max(1, min(all_core_seqs, wp.num_seqs))
     T = n_seqs * L
     cu = np.arange(n_seqs + 1, dtype=np.int32) * L
-    t0 = time.perf_counter()
-    oracle.prefill(wp.q[:T], wp.k[:T], wp.v[:T], wp.g[:T], wp.beta[:T], cu, scale=wp.scale,
-                   export_grid=wp.export_grid)
-    pre_s = time.perf_counter() - t0
+    cores = oracle.num_threads()
+    pre_s, pre_runs = _median_runs(lambda: oracle.prefill(wp.q[:T], wp.k[:T], wp.v[:T], wp.g[:T], wp.beta[:T], cu,
+                                                          scale=wp.scale, export_grid=wp.export_grid))
     B = wd.num_decode_rows
-    si = wd.slot_in
-    compact = wd.pool[si].astype(np.float64)
+    compact = wd.pool[wd.slot_in].astype(np.float64)
     idx = np.arange(B, dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, compact, idx, idx, scale=wd.scale)
-    dec_s = time.perf_counter() - t0
+    dec = lambda: oracle.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, compact.copy(), idx, idx, scale=wd.scale)
+    dec_s, dec_runs = _median_runs(dec)
     dec_bytes = 2 * 4 * wd.d_k * wd.d_v * B * wd.H_v
-    return {"value": round(T / pre_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "prefill of %d of the 16 sequences (%d tokens, all 32 heads, exports on the 1088 grid) "
-                      "in %.1f s; decode of the 64-row batch in %.3f s" % (n_seqs, T, pre_s, dec_s),
-            "decode_state_GB_per_s": round(dec_bytes / dec_s / 1e9, 3)}
+    T1 = min(one_thread_tokens, L)
+    oracle.set_num_threads(1)
+    try:
+        one_s, one_runs = _median_runs(lambda: oracle.prefill(
+            wp.q[:T1], wp.k[:T1], wp.v[:T1], wp.g[:T1], wp.beta[:T1], np.array([0, T1], dtype=np.int32),
+            scale=wp.scale, export_grid=wp.export_grid))
+        dec1_s, dec1_runs = _median_runs(dec)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(T / pre_s, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "prefill of %d of the 16 long sequences (%d tokens, all 32 heads, exports on the 1088 grid), "
+                      "median of %d runs of %.2f s" % (n_seqs, T, pre_runs, pre_s),
+            "decode_state_GB_per_s": round(dec_bytes / dec_s / 1e9, 3),
+            "decode_sample": "the 64-row decode batch, median of %d runs of %.3f s" % (dec_runs, dec_s),
+            "one_thread": {"value": round(T1 / one_s, 1), "unit": "tokens/s", "cores": 1,
+                           "sample": "prefill of the first %d tokens of one long sequence (all 32 heads), median of "
+                                     "%d runs of %.2f s" % (T1, one_runs, one_s),
+                           "decode_state_GB_per_s": round(dec_bytes / dec1_s / 1e9, 3)}}
 
 
 if __name__ == "__main__":

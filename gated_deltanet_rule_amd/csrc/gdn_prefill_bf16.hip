@@ -765,10 +765,32 @@ hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
     return launch_typed<64, 64, HG>(a, stream);
 }
 
+// Compute units of the current device (the launch goes to it), read once per device.
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 }  // namespace
 
+// Two value heads of a key head per workgroup share the K K^T and Q K^T tiles and
+// halve the LDS traffic of staging; one head per workgroup doubles the workgroups.
+// The pair is used only when it still gives every compute unit a workgroup: a call
+// with few sequences (a varlen batch of a few long prompts, the prefill part of a
+// mixed step) is bound by the length of its longest chain, and one head per
+// workgroup runs that chain with four waves on the compute unit instead of eight.
+// Both shapes run the same arithmetic per element, so a sequence's results are
+// bitwise the same whichever shape its call takes.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    if ((a.H_v / a.H_k) % 2 == 0) return launch_dims<2>(a, stream);
+    const int G = a.H_v / a.H_k;
+    if (G % 2 == 0 && (int64_t)a.num_seqs * a.H_k * (G / 2) >= device_cus()) return launch_dims<2>(a, stream);
     return launch_dims<1>(a, stream);
 }
 

@@ -1,5 +1,6 @@
 """Shared helpers for the parity tests: move a workload to the GPU, run the oracle
-on the same values (whole or sampled), and compare element by element."""
+on the same values (one call over the whole workload), and compare element by
+element."""
 from __future__ import annotations
 
 import numpy as np
@@ -39,19 +40,36 @@ def to_device(w: Workload, device="cuda"):
     return d
 
 
-def assert_close(name, got, ref, atol, rtol):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+def assert_close(name, got, ref, atol, rtol, locate=None):
+    """Per-element bound |got - ref| <= atol + rtol |ref| over whole arrays, checked in
+    slices along the first axis so that full-size outputs need no full-size
+    temporaries.  ``locate(index)`` may turn the worst element's index into a
+    readable place (sequence, head, ...)."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     if got.size == 0:
         return
-    assert np.all(np.isfinite(got)), "%s: non-finite values" % name
-    err = np.abs(got - ref)
-    bound = atol + rtol * np.abs(ref)
-    worst = np.unravel_index(np.argmax(err - bound), err.shape)
-    msg = "%s: max abs err %.3g, max err/bound %.3g at %s (got %.6g, ref %.6g)" % (
-        name, err.max(), (err / bound).max(), worst, got[worst], ref[worst])
-    assert np.all(err <= bound), msg
+    n0 = got.shape[0]
+    step = max(1, (1 << 24) // max(1, got.size // n0))
+    worst = (-np.inf, None, 0.0, 0.0, 0.0)       # (err - bound, index, got, ref, err / bound)
+    max_err = 0.0
+    for a in range(0, n0, step):
+        g = np.asarray(got[a:a + step], dtype=np.float64)
+        r = np.asarray(ref[a:a + step], dtype=np.float64)
+        assert np.all(np.isfinite(g)), "%s: non-finite values in rows %d.." % (name, a)
+        err = np.abs(g - r)
+        bound = atol + rtol * np.abs(r)
+        excess = err - bound
+        i = np.unravel_index(np.argmax(excess), excess.shape)
+        max_err = max(max_err, float(err.max()))
+        if excess[i] > worst[0]:
+            idx = (int(i[0]) + a,) + tuple(int(x) for x in i[1:])
+            worst = (float(excess[i]), idx, float(g[i]), float(r[i]), float(err[i] / bound[i]))
+    where = "" if locate is None else " (%s)" % locate(worst[1])
+    msg = "%s: max abs err %.3g, worst err/bound %.3g at %s%s (got %.6g, ref %.6g)" % (
+        name, max_err, worst[4], worst[1], where, worst[2], worst[3])
+    assert worst[0] <= 0.0, msg
 
 
 def decode_reference(w: Workload, rows=None):
@@ -69,35 +87,62 @@ def decode_reference(w: Workload, rows=None):
     return o, compact
 
 
-def prefill_reference(w: Workload, seqs=None, heads=None):
-    """Oracle prefill for (sequence, value head) pairs of the workload's prefill part,
-    one oracle call per pair, several pairs at a time.
-    Returns {(i, h): (o [L, d_v], final [d_k, d_v], exports [n, d_k, d_v])}."""
-    from concurrent.futures import ThreadPoolExecutor
-    B = w.num_decode_rows
-    cu = w.cu_seqlens() + B
-    seqs = range(w.num_seqs) if seqs is None else seqs
-    heads = range(w.H_v) if heads is None else heads
-    G = w.H_v // w.H_k
+class PrefillRef:
+    """The oracle's prefill of a workload's prefill part, every sequence and every
+    value head, from ONE oracle call: o [T_p, H_v, d_v] (prefill tokens only),
+    finals [N, H_v, d_k, d_v], exports [E, H_v, d_k, d_v] and the export offsets.
+    ``ref[(i, h)]`` gives sequence i, head h as (o [L, d_v], final, exports [n, ...])."""
 
-    def one(pair):
-        i, h = pair
-        a, b = int(cu[i]), int(cu[i + 1])
-        sp = None if w.start_pos is None else [int(w.start_pos[i])]
-        kh = h // G
-        init = np.zeros((1, 1, w.d_k, w.d_v))
-        s = int(w.init_slot[i])
-        if 0 <= s < w.pool.shape[0]:
-            init[0, 0] = w.pool[s, h]
-        o, fin, exp_, _ = oracle.prefill(
-            w.q[a:b, kh:kh + 1], w.k[a:b, kh:kh + 1], w.v[a:b, h:h + 1], w.g[a:b, h:h + 1],
-            w.beta[a:b, h:h + 1], np.array([0, b - a]), scale=w.scale, initial_states=init,
+    def __init__(self, w: Workload):
+        B = w.num_decode_rows
+        N = w.num_seqs
+        init = np.zeros((N, w.H_v, w.d_k, w.d_v), dtype=np.float64)
+        for i in range(N):
+            s = int(w.init_slot[i])
+            if 0 <= s < w.pool.shape[0]:
+                init[i] = w.pool[s]
+        self.cu = w.cu_seqlens()
+        sp = None if w.start_pos is None else np.asarray(w.start_pos)
+        self.o, self.finals, self.exports, self.offsets = oracle.prefill(
+            w.q[B:], w.k[B:], w.v[B:], w.g[B:], w.beta[B:], self.cu, scale=w.scale, initial_states=init,
             start_pos=sp, export_grid=w.export_grid)
-        return pair, (o[:, 0], fin[0, 0], exp_[:, 0])
 
-    pairs = [(i, h) for i in seqs for h in heads]
-    with ThreadPoolExecutor(max_workers=min(16, max(1, len(pairs)))) as ex:
-        return dict(ex.map(one, pairs))
+    def __getitem__(self, key):
+        i, h = key
+        a, b = int(self.cu[i]), int(self.cu[i + 1])
+        return (self.o[a:b, h], self.finals[i, h],
+                self.exports[int(self.offsets[i]):int(self.offsets[i + 1]), h])
+
+    def seq_of_token(self, t):
+        return int(np.searchsorted(self.cu, t, side="right") - 1)
+
+
+def prefill_reference(w: Workload) -> PrefillRef:
+    return PrefillRef(w)
+
+
+def check_prefill(w: Workload, ref: PrefillRef, o, pool, exports=None, tag=""):
+    """Every output row, final state and export of the workload's prefill part
+    against the oracle, within the dtype's bound.  ``o`` holds the prefill tokens
+    only; ``pool`` holds the final states at w.final_slot; ``exports`` the flat export
+    stream (or None when the call exported nothing)."""
+    atol, rtol = TOL[w.dtype]
+    got_o = o.float().cpu().numpy()
+    assert_close(tag + "o", got_o, ref.o, atol, rtol,
+                 locate=lambda ix: "sequence %d, token %d, head %d" % (
+                     ref.seq_of_token(ix[0]), ix[0] - int(ref.cu[ref.seq_of_token(ix[0])]), ix[1]))
+    valid = [i for i in range(w.num_seqs) if 0 <= int(w.final_slot[i]) < w.pool.shape[0]]
+    if valid:
+        slots = torch.as_tensor([int(w.final_slot[i]) for i in valid], dtype=torch.long, device=pool.device)
+        assert_close(tag + "final states", pool[slots].cpu().numpy(), ref.finals[valid], atol, rtol,
+                     locate=lambda ix: "sequence %d, head %d" % (valid[ix[0]], ix[1]))
+    if w.export_grid:
+        E = int(ref.offsets[-1])
+        assert exports is not None or E == 0
+        if E:
+            assert_close(tag + "exports", exports[:E].cpu().numpy(), ref.exports, atol, rtol,
+                         locate=lambda ix: "export %d (sequence %d), head %d" % (
+                             ix[0], int(np.searchsorted(ref.offsets, ix[0], side="right") - 1), ix[1]))
 
 
 def run_prefill(w: Workload, d, export=True, stream=None):

@@ -1,5 +1,6 @@
-"""Chunked prefill on the GPU: parity with the fp64 oracle (whole for small cases,
-sampled (sequence, head) chains at full size), exported states on the grid,
+"""Chunked prefill on the GPU: parity with the fp64 oracle on every output row, final
+state and export (one oracle call per workload, full-size workloads included),
+exported states on the grid,
 resume from an exported state, per-sequence batch invariance, slot semantics and
 determinism.
 
@@ -14,29 +15,9 @@ import torch
 
 from gated_deltanet_rule_amd import binding
 from gated_deltanet_rule_amd import workloads as W
-from tests.helpers import TOL, assert_close, prefill_reference, run_prefill, to_device
+from tests.helpers import check_prefill, prefill_reference, run_prefill, to_device
 
 pytestmark = pytest.mark.gpu
-
-
-def _check(w, d, exp_states, ref, seqs=None, heads=None):
-    atol, rtol = TOL[w.dtype]
-    cu = w.cu_seqlens()
-    seqs = range(w.num_seqs) if seqs is None else seqs
-    heads = range(w.H_v) if heads is None else heads
-    o = d["o"].float()
-    offs = binding.export_offsets(w.lengths, None if w.start_pos is None else list(w.start_pos), w.export_grid)
-    for i in seqs:
-        a, b = int(cu[i]), int(cu[i + 1])
-        fs = int(w.final_slot[i])
-        for h in heads:
-            ro, rf, rexp = ref[(i, h)]
-            assert_close("o seq %d head %d" % (i, h), o[a:b, h].cpu().numpy(), ro, atol, rtol)
-            assert_close("final seq %d head %d" % (i, h), d["pool"][fs, h].cpu().numpy(), rf, atol, rtol)
-            if w.export_grid:
-                got = exp_states[offs[i]:offs[i + 1], h].cpu().numpy()
-                assert got.shape[0] == rexp.shape[0]
-                assert_close("exports seq %d head %d" % (i, h), got, rexp, atol, rtol)
 
 
 def test_prefill_single_sequence_fp32():
@@ -45,7 +26,7 @@ def test_prefill_single_sequence_fp32():
     d = to_device(w)
     exp_states, _ = run_prefill(w, d)
     torch.cuda.synchronize()
-    _check(w, d, exp_states, prefill_reference(w))
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
 
 
 @pytest.mark.parametrize("dtype,dk,dv,hk,hv", [("bf16", 128, 128, 2, 4), ("f32", 64, 64, 1, 2),
@@ -69,7 +50,7 @@ def test_prefill_varlen_ragged(dtype, dk, dv, hk, hv):
     d = to_device(w)
     exp_states, _ = run_prefill(w, d)
     torch.cuda.synchronize()
-    _check(w, d, exp_states, prefill_reference(w))
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
 
 
 @pytest.mark.parametrize("dtype,dk,dv,hk,hv,key_mix,gate_scale,beta_shift", [
@@ -97,7 +78,7 @@ def test_prefill_stress_inputs(dtype, dk, dv, hk, hv, key_mix, gate_scale, beta_
     d = to_device(w)
     exp_states, _ = run_prefill(w, d)
     torch.cuda.synchronize()
-    _check(w, d, exp_states, prefill_reference(w))
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
 
 
 def test_prefill_canaries():
@@ -170,6 +151,45 @@ def test_prefill_batch_invariance():
         assert torch.equal(exp_solo[:n_i], exp_all[offs[i]:offs[i + 1]]), i
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
+    """With two value heads per key head the bf16 kernel gives each workgroup both
+    heads when the call has enough (sequence, key head) pairs to fill the compute
+    units, and one head otherwise.  The same sequences alone (few pairs: one head per
+    workgroup) and inside a batch that fills the GPU (two heads per workgroup) give
+    bitwise equal outputs, final states and exports."""
+    H_k, H_v = 16, 32
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = -(-cus // H_k)                               # sequences for a full launch of head pairs
+    rng = np.random.default_rng(33)
+    lengths = [int(x) for x in rng.integers(1, 400, size=n)]
+    lengths[0], lengths[-1] = 333, 130
+    base = W.make_workload("shape", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=lengths,
+                           num_slots=2 * n + 4, prefill_init="slots", export_grid=64)
+    dbase = to_device(base)
+    exp_all, _ = run_prefill(base, dbase)
+    cu = base.cu_seqlens()
+    offs = binding.export_offsets(base.lengths, None, 64)
+    for i in (0, n // 2, n - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        solo = W.make_workload("shape1", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=[b - a],
+                               num_slots=2 * n + 4, export_grid=64)
+        for name in ("q", "k", "v", "g", "beta"):
+            setattr(solo, name, getattr(base, name)[a:b].copy())
+        solo.pool = base.pool
+        solo.init_slot = base.init_slot[i:i + 1].copy()
+        solo.final_slot = np.array([2 * n + 3], dtype=np.int32)
+        dsolo = to_device(solo)
+        exp_solo, _ = run_prefill(solo, dsolo)
+        torch.cuda.synchronize()
+        assert torch.equal(dsolo["o"], dbase["o"][a:b]), i
+        assert torch.equal(dsolo["pool"][2 * n + 3], dbase["pool"][int(base.final_slot[i])]), i
+        n_i = offs[i + 1] - offs[i]
+        assert torch.equal(exp_solo[:n_i], exp_all[offs[i]:offs[i + 1]]), i
+    # and the full batch against the oracle
+    check_prefill(base, prefill_reference(base), dbase["o"], dbase["pool"], exp_all)
+
+
 def test_prefill_deterministic():
     w = W.make_workload("det", seed=25, H_k=2, H_v=4, d_k=128, d_v=128, dtype="bf16",
                         lengths=[700, 129, 64], num_slots=16, export_grid=128)
@@ -184,27 +204,26 @@ def test_prefill_deterministic():
             assert all(torch.equal(x, y) for x, y in zip(snap, first))
 
 
-def test_prefill_cfg2_sampled():
+def test_prefill_cfg2_full():
     """The varlen batch (8 sequences, lengths in [64, 4096], 16/32 heads, d = 128,
-    bf16, exports every 64 tokens) at full size; the oracle checks sampled chains."""
+    bf16, exports every 64 tokens) at full size: every output row, final state and
+    export of every (sequence, value head) chain against one oracle call."""
     w = W.config(2, fill_pool=False)
     d = to_device(w)
     exp_states, _ = run_prefill(w, d)
     torch.cuda.synchronize()
-    seqs, heads = [0, 3, 7], [0, 13, 31]
-    _check(w, d, exp_states, prefill_reference(w, seqs, heads), seqs, heads)
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
 
 
-def test_prefill_cfg4_sampled_and_resume():
-    """Long prefill (16 x 8192, export grid 1088 = lcm(64, 1088)) at full size: sampled
-    chains against the oracle, then a resume from the exported state at 4352 = 4 x 1088
-    reproduces the rest of the run bitwise."""
+def test_prefill_cfg4_full_and_resume():
+    """Long prefill (16 x 8192, export grid 1088 = lcm(64, 1088)) at full size: every
+    chain against one oracle call, then a resume from the exported state at 4352 =
+    4 x 1088 reproduces the rest of the run bitwise."""
     w = W.config(4, fill_pool=False)
     d = to_device(w)
     exp_states, exp_offs = run_prefill(w, d)
     torch.cuda.synchronize()
-    seqs, heads = [0, 9], [5, 30]
-    _check(w, d, exp_states, prefill_reference(w, seqs, heads), seqs, heads)
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
     full_o, full_pool = d["o"].clone(), d["pool"].clone()
     # resume every sequence at 4352 from its 4th exported state (index 3)
     cut = 4352
@@ -244,8 +263,7 @@ def test_prefix_cache_grid_cases():
     exp_states, _ = run_prefill(w, d)
     torch.cuda.synchronize()
     assert exp_states.shape[0] == 1                      # 2000 tokens cross one grid point
-    ref = prefill_reference(w)
-    _check(w, d, exp_states, ref)
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"], exp_states)
     hit = (1100 // grid) * grid
     assert hit == 1088 and (200 // grid) * grid == 0
     pool = d["pool"].clone()
@@ -287,4 +305,4 @@ def test_prefill_zero_length_and_empty():
     torch.cuda.synchronize()
     for i in (0, 2):
         assert torch.equal(d["pool"][int(w.final_slot[i])].cpu(), torch.from_numpy(w.pool[int(w.init_slot[i])]))
-    _check(w, d, None, prefill_reference(w, [1]), [1])
+    check_prefill(w, prefill_reference(w), d["o"], d["pool"])

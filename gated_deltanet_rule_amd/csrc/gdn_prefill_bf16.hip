@@ -163,7 +163,7 @@ __device__ __forceinline__ constexpr int blk(int i, int j) { return i * (i + 1) 
 // three factors of at most 1.
 enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, GATE_FS = 4, GATE_TE = 5, kGates = 6 };
 
-template <int DK, int DV, int HG>
+template <int DK, int DV, int HG, int KB>
 struct Smem {
     // Q and K rows (bf16).  The pitch is an odd multiple of 8 dwords and row r keeps
     // its 16-byte column groups swizzled, column c at c ^ (r & 8): with that, the
@@ -180,8 +180,9 @@ struct Smem {
     static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
     static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
     __bf16 q[kC * QLD];
-    __bf16 k[2][kC * QLD];                    // by chunk parity (the state update of chunk
-                                              // c reads it while chunk c+1 is staged)
+    __bf16 k[KB][kC * QLD];                   // two: by chunk parity (the state update of
+                                              // chunk c reads it while chunk c+1 is
+                                              // staged); one: staged after the update
     struct Head {
         __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
         __bf16 p[10][2][BSZ];                 // P blocks; hi, lo
@@ -196,9 +197,9 @@ __device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
     j = t - i * (i + 1) / 2;
 }
 
-template <int DK, int DV, int HG>
-__global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
-    using SM = Smem<DK, DV, HG>;
+template <int DK, int DV, int HG, int KB>
+__global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs a) {
+    using SM = Smem<DK, DV, HG, KB>;
     constexpr int NWH = DV / 32;             // waves per value head
     constexpr int NW = HG * NWH;             // waves
     constexpr int NT = NW * 64;              // threads
@@ -330,20 +331,18 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
                 pv[mt][nt] = (int)r < L ? *reinterpret_cast<const bf16x4*>(vb + off) : bf16x4{};
             }
     };
-    // Write chunk c's prefetched Q and K rows and the gates (those two by chunk parity)
-    // to LDS.  For chunk c + 1 this runs right after the barrier that ends phase 1 of
-    // chunk c: Q was last read in phase 1, and the other parity of K and the gates was
-    // last read in phase 3 of chunk c - 1.  Doing it before phase 3 issues its stores
-    // keeps the wait for the loads from waiting for those.
-    auto stage_qk = [&](int c, unsigned t) {
-        __bf16* kb = sm.k[c & 1];
+    // Write chunk c's prefetched Q rows and gates (by chunk parity) to LDS.  For chunk
+    // c + 1 this runs right after the barrier that ends phase 1 of chunk c: Q was last
+    // read in phase 1, and the other parity of the gates was last read in phase 3 of
+    // chunk c - 1.  Doing it before phase 3 issues its stores keeps the wait for the
+    // loads from waiting for those.
+    auto stage_q = [&](int c, unsigned t) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const unsigned i = t + NT * j;
             const unsigned r = i / VPR, vi = i % VPR;
             const unsigned col = (vi * 8) ^ (r & 8);
             *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = pq[j];
-            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = pk[j];
         }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
@@ -363,12 +362,26 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
             gt[GATE_TE * kC + ln] = __builtin_amdgcn_exp2f(G2_be - G2);
         }
     };
+    // Chunk c's prefetched K rows: with two buffers, into the other parity at the same
+    // point as Q (the state update of chunk c - 1 was its last reader); with one, after
+    // the barrier that follows chunk c - 1's state update.
+    auto stage_k = [&](int c, unsigned t) {
+        __bf16* kb = sm.k[KB == 2 ? (c & 1) : 0];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const unsigned i = t + NT * j;
+            const unsigned r = i / VPR, vi = i % VPR;
+            const unsigned col = (vi * 8) ^ (r & 8);
+            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = pk[j];
+        }
+    };
     // Q and K loads run a chunk ahead of their staging: right after phase 1 of chunk
     // c, chunk c + 1's Q and K rows are staged; chunk c + 2's are fetched at the end of
     // chunk c's phase 3, after chunk c + 1's V strip (used in phase 1 of chunk c + 1).
     if (nchunks > 0) {
         prefetch_qk(0, (unsigned)tid);
-        stage_qk(0, (unsigned)tid);
+        stage_q(0, (unsigned)tid);
+        stage_k(0, (unsigned)tid);
         prefetch_v(0, lane);
         if (nchunks > 1) prefetch_qk(1, (unsigned)tid);
     }
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         int tid_l = tid;
         asm volatile("" : "+v"(lane), "+v"(tid_l));
         const int li = lane & 15, g4 = lane >> 4;
-        const __bf16* kb = sm.k[buf];
+        const __bf16* kb = sm.k[KB == 2 ? buf : 0];
 
         dev::lds_barrier();
 
@@ -556,7 +569,10 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         // here its loads have all of phase 3 to land
         if (c + 1 < nchunks) prefetch_v(c + 1, lane);
         dev::lds_barrier();   // every -A_ij, T_ii and P block is complete
-        if (c + 1 < nchunks) stage_qk(c + 1, (unsigned)tid_l);
+        if (c + 1 < nchunks) {
+            stage_q(c + 1, (unsigned)tid_l);
+            if (KB == 2) stage_k(c + 1, (unsigned)tid_l);
+        }
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
@@ -702,6 +718,11 @@ __global__ __launch_bounds__(HG * DV * 2) void chunk_kernel(PrefillArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        // One K buffer: every wave's state update has read it once all pass the barrier.
+        if (KB == 1 && c + 1 < nchunks) {
+            dev::lds_barrier();
+            stage_k(c + 1, (unsigned)tid_l);
+        }
         // Chunk c + 2's loads go out here, after the state update: issued together with
         // the staging at the start of phase 3, their burst delayed the solve.
         if (c + 2 < nchunks) prefetch_qk(c + 2, (unsigned)tid_l);
@@ -753,7 +774,8 @@ template <int DK, int DV, int HG>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const int G = a.H_v / a.H_k;
     const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG);
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG>), dim3(blocks), dim3(HG * DV * 2), 0, stream, a);
+    constexpr int KB = HG == 1 ? 1 : 2;
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG, KB>), dim3(blocks), dim3(HG * DV * 2), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -40,15 +40,23 @@
 //   phase 3  per strip: the block solve for U, each output row block as soon as
 //            its U blocks exist, then the state update (K^T read from the K rows
 //            by transposing LDS reads) and the grid export
-// Precision.  All products are bf16 MFMA with fp32 accumulation.  q, k and v enter
-// exactly; S and Z enter as single bf16 values; every other operand -- the -A_ij,
-// T_ii and P blocks, the right-hand sides, U and the decayed U -- enters as a hi +
-// lo pair of bf16 values (x = hi + lo to about 2^-17) in three products (hi hi,
-// hi lo, lo hi) or two when the other side is exact.  Gates, the A_ii inverses and
-// all accumulators are fp32.  A sequence's work never depends on the other
-// sequences of the call, so its results are bitwise
-// independent of its batch-mates; chunks lie on the absolute 64-token grid, so a
-// resume from an exported grid state continues with the same arithmetic.
+// Precision.  Products run on the matrix cores with fp32 accumulation, in two 16-bit
+// formats.  q and k are staged in LDS as fp16 (exact for the normalised keys and
+// queries of the rule, down to 2^-24 below fp16's normal range), and every product
+// with Q, K or K^T is an fp16 one: K K^T, Q K^T, Z = K S and Q S with S rounded once
+// to fp16, and the state update with the decayed U as an fp16 hi + lo pair.  The
+// output product takes P and U as single fp16 values, and so does T_ii X_i.  The
+// off-diagonal solve products -A_ij U_j take both sides as bf16 hi + lo pairs (x =
+// hi + lo to about 2^-17) in three products, and V enters exactly through a bf16
+// identity product.  fp16 has four times bf16's precision, which is what lets single
+// roundings stand where bf16 needed pairs; its range bounds the values: states,
+// values and outputs must stay below 2^15 in magnitude.  Gates, the A_ii inverses
+// and all accumulators are fp32.  A sequence's work never depends on the other
+// sequences of the call, so its results are bitwise independent of its batch-mates;
+// chunks lie on the absolute 64-token grid, so a resume from an exported grid state
+// continues with the same arithmetic, and a partial last chunk gives its rows the
+// bits the full chunk would (a row combines only rows at or before it; padding rows
+// enter as exact zeros).
 #include <hip/hip_runtime.h>
 
 #include "gdn_device.h"
@@ -64,6 +72,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- MFMA operands
 //
@@ -80,6 +91,12 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
                                                      c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16h(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 struct Split4 { bf16x4 hi, lo; };
@@ -120,37 +137,78 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return r;
 }
 
+// fp16 values are moved as whole 32-bit words (bit casts of packed pairs), never as
+// single 16-bit lanes: this compiler merged two 16-bit stores of one pair into a
+// pack of the low half twice.
+__device__ __forceinline__ f16x8 cat8h(f16x4 a, f16x4 b) {
+    const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+    return __builtin_bit_cast(f16x8, make_uint4(x.x, x.y, y.x, y.y));
+}
+
+// four fp32 values rounded to fp16 (round to nearest even, two per instruction)
+__device__ __forceinline__ f16x4 cvt4h(f32x4 x) {
+    const f16x2 a = __builtin_convertvector((f32x2{x[0], x[1]}), f16x2);
+    const f16x2 b = __builtin_convertvector((f32x2{x[2], x[3]}), f16x2);
+    return __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)));
+}
+
+struct Split4h { f16x4 hi, lo; };
+
+// x = hi + lo in fp16: hi rounded, lo the remainder x - hi (from one fp16 dot product
+// per value, exact while hi is a normal fp16) rounded once; x = hi + lo to about
+// 2^-22.  The (-1, 0) pairs are made in SGPRs, as for the bf16 split.
+__device__ __forceinline__ Split4h split4h(f32x4 x) {
+    const f16x2 h01 = __builtin_convertvector((f32x2{x[0], x[1]}), f16x2);
+    const f16x2 h23 = __builtin_convertvector((f32x2{x[2], x[3]}), f16x2);
+    unsigned c0, c1;
+    asm("s_mov_b32 %0, 0xbc00" : "=s"(c0));       // fp16 pair (-1, 0)
+    asm("s_mov_b32 %0, 0xbc000000" : "=s"(c1));   // fp16 pair (0, -1)
+    const f16x2 m0 = __builtin_bit_cast(f16x2, c0), m1 = __builtin_bit_cast(f16x2, c1);
+    const f32x2 r01 = {__builtin_amdgcn_fdot2(h01, m0, x[0], false), __builtin_amdgcn_fdot2(h01, m1, x[1], false)};
+    const f32x2 r23 = {__builtin_amdgcn_fdot2(h23, m0, x[2], false), __builtin_amdgcn_fdot2(h23, m1, x[3], false)};
+    const f16x2 l01 = __builtin_convertvector(r01, f16x2);
+    const f16x2 l23 = __builtin_convertvector(r23, f16x2);
+    Split4h s;
+    s.hi = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, h01), __builtin_bit_cast(unsigned, h23)));
+    s.lo = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, l01), __builtin_bit_cast(unsigned, l23)));
+    return s;
+}
+
+// a bf16 pair widened and rounded to an fp16 pair (the 32-bit word in, the word out)
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w) {
+    const f32x2 x = {__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, f16x2));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w) {
+    return make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w));
+}
+
 __device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ void st4(__bf16* p, bf16x4 x) { *reinterpret_cast<bf16x4*>(p) = x; }
+__device__ __forceinline__ f16x4 ld4h(const _Float16* p) { return *reinterpret_cast<const f16x4*>(p); }
+__device__ __forceinline__ f16x8 ld8h(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ void st4h(_Float16* p, f16x4 x) { *reinterpret_cast<f16x4*>(p) = x; }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
 // 16 g + i receives element e = 0..3 from the address of lane 16 g + 4 e + i / 4, at
 // position i % 4 of that lane's four values.  So if lane l points at row r0 + l / 4,
-// columns c0 + 4 (l % 4) of a row-major bf16 matrix M, lane 16 g + i gets
+// columns c0 + 4 (l % 4) of a row-major 16-bit matrix M, lane 16 g + i gets
 // M[r0 + 4 g + e][c0 + i]: the A operand of M^T (row i, k = 4 g + e) in one read.
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-__device__ __forceinline__ bf16x4 ld4_tr(const __bf16* p) {
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+__device__ __forceinline__ f16x4 ld4_tr(const _Float16* p) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
 // 16x32 operand of a row-major Q or K row in LDS, k from 32 ks in from-C order; sw is
 // the row's column swizzle (see Smem)
-__device__ __forceinline__ bf16x8 row_fromc(const __bf16* row, int ks, int g, int sw) {
-    const __bf16* p = row + ((4 * g) ^ sw);    // the swizzle only touches column bit 3
-    return cat8(ld4(p + 32 * ks), ld4(p + 32 * ks + 16));
+__device__ __forceinline__ f16x8 row_fromc(const _Float16* row, int ks, int g, int sw) {
+    const _Float16* p = row + ((4 * g) ^ sw);  // the swizzle only touches column bit 3
+    return cat8h(ld4h(p + 32 * ks), ld4h(p + 32 * ks + 16));
 }
 
-// B operand (from-C order, k step ks) out of a pair of state accumulator tiles
-__device__ __forceinline__ bf16x8 state_frag(const f32x4& t0, const f32x4& t1) {
-    const bf16x2 a = __builtin_convertvector(f32x2{t0[0], t0[1]}, bf16x2);
-    const bf16x2 b = __builtin_convertvector(f32x2{t0[2], t0[3]}, bf16x2);
-    const bf16x2 c = __builtin_convertvector(f32x2{t1[0], t1[1]}, bf16x2);
-    const bf16x2 d = __builtin_convertvector(f32x2{t1[2], t1[3]}, bf16x2);
-    bf16x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-    return r;
+// B operand (from-C order, k step ks) out of a pair of state accumulator tiles, in fp16
+__device__ __forceinline__ f16x8 state_frag(const f32x4& t0, const f32x4& t1) {
+    return cat8h(cvt4h(t0), cvt4h(t1));
 }
 
 // Lower 16x16 blocks (i, j), j <= i, of a 64x64 matrix, numbered row by row.
@@ -165,13 +223,13 @@ enum { GATE_G2 = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, GATE_FS = 4, GATE
 
 template <int DK, int DV, int HG, int KB>
 struct Smem {
-    // Q and K rows (bf16).  The pitch is an odd multiple of 8 dwords and row r keeps
+    // Q and K rows (fp16).  The pitch is an odd multiple of 8 dwords and row r keeps
     // its 16-byte column groups swizzled, column c at c ^ (r & 8): with that, the
     // row-fragment reads (16 rows, one column group each), the transposing reads
     // (8 rows x 32 bytes per half wave) and the staging writes all hit distinct
     // banks.
     static constexpr int QLD = DK + 16;
-    static constexpr int BLD = 24;            // rows of a 16x16 bf16 block (12 dwords:
+    static constexpr int BLD = 24;            // rows of a 16x16 16-bit block (12 dwords:
                                               // a half wave's 8-byte row reads are
                                               // bank-conflict free)
     // block stride: 8 bf16 of padding put the four diagonal blocks (slots 0, 2, 5, 9),
@@ -179,13 +237,14 @@ struct Smem {
     static constexpr int BSZ = 16 * BLD + 8;
     static constexpr int ATLD = 20;           // rows of a transposed fp32 A_ii block
     static constexpr int ATB = 16 * ATLD + 4; // block stride (spreads the four blocks over banks)
-    __bf16 q[kC * QLD];
-    __bf16 k[KB][kC * QLD];                   // two: by chunk parity (the state update of
+    _Float16 q[kC * QLD];
+    _Float16 k[KB][kC * QLD];                   // two: by chunk parity (the state update of
                                               // chunk c reads it while chunk c+1 is
                                               // staged); one: staged after the update
     struct Head {
-        __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i) or T_ii; hi, lo
-        __bf16 p[10][2][BSZ];                 // P blocks; hi, lo
+        __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i), bf16 hi, lo; or
+                                              // T_ii, fp16, in the hi slot
+        _Float16 p[10][BSZ];                  // P blocks (fp16)
         float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
         float gate[2][kGates * kC];           // by chunk parity
     } hd[HG];
@@ -342,7 +401,7 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
             const unsigned i = t + NT * j;
             const unsigned r = i / VPR, vi = i % VPR;
             const unsigned col = (vi * 8) ^ (r & 8);
-            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = pq[j];
+            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = bf16x8_to_f16x8(pq[j]);
         }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
@@ -366,13 +425,13 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
     // point as Q (the state update of chunk c - 1 was its last reader); with one, after
     // the barrier that follows chunk c - 1's state update.
     auto stage_k = [&](int c, unsigned t) {
-        __bf16* kb = sm.k[KB == 2 ? (c & 1) : 0];
+        _Float16* kb = sm.k[KB == 2 ? (c & 1) : 0];
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const unsigned i = t + NT * j;
             const unsigned r = i / VPR, vi = i % VPR;
             const unsigned col = (vi * 8) ^ (r & 8);
-            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = pk[j];
+            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = bf16x8_to_f16x8(pk[j]);
         }
     };
     // Q and K loads run a chunk ahead of their staging: right after phase 1 of chunk
@@ -396,7 +455,7 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
         int tid_l = tid;
         asm volatile("" : "+v"(lane), "+v"(tid_l));
         const int li = lane & 15, g4 = lane >> 4;
-        const __bf16* kb = sm.k[KB == 2 ? buf : 0];
+        const _Float16* kb = sm.k[KB == 2 ? buf : 0];
 
         dev::lds_barrier();
 
@@ -409,12 +468,12 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
             const float* gt = hd.gate[buf];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                bf16x8 kf[KS_DK];             // both operands are this block's K rows
+                f16x8 kf[KS_DK];              // both operands are this block's K rows
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8(kb + (16 * b + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
+                for (int kk = 0; kk < KS_DK; ++kk) kf[kk] = ld8h(kb + (16 * b + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(kf[kk], kf[kk], acc);
+                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32h(kf[kk], kf[kk], acc);
                 const int r = 16 * b + li, s0 = 16 * b + 4 * g4;
                 const float G2r = gt[GATE_G2 * kC + r];
                 const float br = gt[GATE_BET * kC + r];
@@ -453,13 +512,12 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int bb = (0x9520 >> (4 * b)) & 15;   // blk(b, b) for b = 0..3
-            __bf16* th = hd.sol[bb][0];
-            __bf16* tl = hd.sol[bb][1];
+            unsigned short* th = reinterpret_cast<unsigned short*>(hd.sol[bb][0]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const __bf16 x = (__bf16)t[r];
-                th[r * SM::BLD + jc] = x;
-                tl[r * SM::BLD + jc] = (__bf16)(t[r] - (float)x);
+            for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 from one packed pair
+                const unsigned w = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{t[r], t[r + 1]}), f16x2));
+                th[r * SM::BLD + jc] = (unsigned short)(w & 0xffffu);
+                th[(r + 1) * SM::BLD + jc] = (unsigned short)(w >> 16);
             }
         } else {
             constexpr int NTI = (16 + NNL - 1) / NNL;
@@ -475,16 +533,16 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                 } else {
                     tile_ij(tt - 6, i, j);
                 }
-                const __bf16* X = tt < 6 ? kb : sm.q;
-                bf16x8 fa[KS_DK], fb[KS_DK];
+                const _Float16* X = tt < 6 ? kb : sm.q;
+                f16x8 fa[KS_DK], fb[KS_DK];
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    fa[kk] = ld8(kb + (16 * j + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
-                    fb[kk] = ld8(X + (16 * i + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
+                    fa[kk] = ld8h(kb + (16 * j + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
+                    fb[kk] = ld8h(X + (16 * i + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32(fa[kk], fb[kk], acc);
+                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32h(fa[kk], fb[kk], acc);
                 // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
                 const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
 #pragma unroll
@@ -502,9 +560,7 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                             st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
                             st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
                         } else {
-                            const Split4 sp = split4(acc * te * (a.scale * fr));
-                            st4(hx.p[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
-                            st4(hx.p[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                            st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(acc * te * (a.scale * fr)));
                         }
                     } else {                     // a diagonal block of Q K^T: s <= r only
                         const float G2r = gx[GATE_G2 * kC + r];
@@ -513,9 +569,7 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             pd[e] = s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f;
-                        const Split4 sp = split4(pd);
-                        st4(hx.p[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
-                        st4(hx.p[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                        st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(pd));
                     }
                 }
             }
@@ -527,7 +581,7 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
         const float* gt = hd.gate[buf];
         f32x4 Racc[4][2], Oacc[4][2];
         {
-            bf16x8 Sb[KS_DK][2];
+            f16x8 Sb[KS_DK][2];
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk)
 #pragma unroll
@@ -537,12 +591,12 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                 Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    const bf16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
-                    const bf16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
+                    const f16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
+                    const f16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
-                        Racc[mt][nt] = mma32(ak, Sb[kk][nt], Racc[mt][nt]);
-                        Oacc[mt][nt] = mma32(Sb[kk][nt], aq, Oacc[mt][nt]);
+                        Racc[mt][nt] = mma32h(ak, Sb[kk][nt], Racc[mt][nt]);
+                        Oacc[mt][nt] = mma32h(Sb[kk][nt], aq, Oacc[mt][nt]);
                     }
                 }
             }
@@ -577,7 +631,8 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
-        Split4 Us[4][2];
+        Split4 Us[4][2];                     // U blocks as bf16 pairs (the solve)
+        f16x4 Uh[4][2];                      // and as single fp16 values (the output product)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -609,48 +664,26 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                     X = mma32(a2, cat8(Us[j][nt].hi, Us[j][nt].hi), X);
                     X = mma32(a2, cat8(Us[j][nt].lo, Us[j][nt].lo), X);
                 }
-                const Split4 xs = split4(X);
-                const bf16x4 th = ld4(hd.sol[blk(i, i)][0] + li * SM::BLD + 4 * g4);
-                const bf16x4 tl = ld4(hd.sol[blk(i, i)][1] + li * SM::BLD + 4 * g4);
-                f32x4 U = mma16(th, xs.hi, f32x4{0.f, 0.f, 0.f, 0.f});
-                U = mma16(th, xs.lo, U);
-                U = mma16(tl, xs.hi, U);
+                // U_i = T_ii X_i, both single fp16 values
+                const f16x4 th = ld4h(reinterpret_cast<const _Float16*>(hd.sol[blk(i, i)][0]) + li * SM::BLD + 4 * g4);
+                const f32x4 U = mma16h(th, cvt4h(X), f32x4{0.f, 0.f, 0.f, 0.f});
                 Racc[i][nt] = U;
                 Us[i][nt] = split4(U);
+                Uh[i][nt] = cvt4h(U);
             }
-            // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, blocks in pairs.
-            // U and P both enter as hi + lo pairs (three products): when keys are highly
-            // correlated and gates near zero, U grows large and O is a small difference of
-            // large terms, where a single bf16 rounding of either side is too coarse.
-            // A block pair takes three 16x16x32 products; a last single block (even i)
-            // takes two, hi and lo of U side by side against P's hi twice, then against
-            // P's lo twice.
+            // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, U and P as
+            // single fp16 values, blocks in pairs on 16x16x32 products; a last single
+            // block (even i) on one 16x16x32 product too, with a zero P half (every
+            // product that accumulates into O has one shape).
+            const f16x4 zero4 = {};
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
                 const int j0 = 2 * kk, j1 = 2 * kk + 1;
-                const bf16x4 ph0 = ld4(hd.p[blk(i, j0)][0] + li * SM::BLD + 4 * g4);
-                const bf16x4 pl0 = ld4(hd.p[blk(i, j0)][1] + li * SM::BLD + 4 * g4);
-                if (j1 <= i) {
-                    const bf16x8 ph = cat8(ph0, ld4(hd.p[blk(i, j1)][0] + li * SM::BLD + 4 * g4));
-                    const bf16x8 pl = cat8(pl0, ld4(hd.p[blk(i, j1)][1] + li * SM::BLD + 4 * g4));
+                const f16x4 p0 = ld4h(hd.p[blk(i, j0)] + li * SM::BLD + 4 * g4);
+                const f16x8 pp = cat8h(p0, j1 <= i ? ld4h(hd.p[blk(i, j1)] + li * SM::BLD + 4 * g4) : zero4);
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const bf16x8 uh = cat8(Us[j0][nt].hi, Us[j1][nt].hi);
-                        const bf16x8 ul = cat8(Us[j0][nt].lo, Us[j1][nt].lo);
-                        Oacc[i][nt] = mma32(uh, ph, Oacc[i][nt]);
-                        Oacc[i][nt] = mma32(ul, ph, Oacc[i][nt]);
-                        Oacc[i][nt] = mma32(uh, pl, Oacc[i][nt]);
-                    }
-                } else {
-                    const bf16x8 pp = cat8(ph0, ph0);
-                    const bf16x8 pl = cat8(pl0, pl0);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const bf16x8 u2 = cat8(Us[j0][nt].hi, Us[j0][nt].lo);
-                        Oacc[i][nt] = mma32(u2, pp, Oacc[i][nt]);
-                        Oacc[i][nt] = mma32(u2, pl, Oacc[i][nt]);
-                    }
-                }
+                for (int nt = 0; nt < 2; ++nt)
+                    Oacc[i][nt] = mma32h(cat8h(Uh[j0][nt], Uh[j1 <= i ? j1 : j0][nt]), pp, Oacc[i][nt]);
             }
             // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap
             // between lane groups g4 and g4 ^ 1 (v_permlane16_swap: rows 1 and 3 of the
@@ -673,31 +706,31 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
         // S += K^T (diag(e^(G_last - G)) U), token blocks in pairs.  The B operands
         // first; then the K^T reads (transposing reads of the K rows) run two steps
         // ahead of the MFMAs that use them.
-        const __bf16* ktr = kb + (lane >> 2) * SM::QLD + ((4 * (lane & 3)) ^ ((lane >> 2) & 8));
-        bf16x8 bh[2][2], bl[2][2];
+        const _Float16* ktr = kb + (lane >> 2) * SM::QLD + ((4 * (lane & 3)) ^ ((lane >> 2) & 8));
+        f16x8 bh[2][2], bl[2][2];            // the decayed U as fp16 hi + lo pairs
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const f32x4 kd0 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 4 * g4);
             const f32x4 kd1 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 16 + 4 * g4);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const Split4 s0 = split4(Racc[2 * kk][nt] * kd0);
-                const Split4 s1 = split4(Racc[2 * kk + 1][nt] * kd1);
-                bh[kk][nt] = cat8(s0.hi, s1.hi);
-                bl[kk][nt] = cat8(s0.lo, s1.lo);
+                const Split4h s0 = split4h(Racc[2 * kk][nt] * kd0);
+                const Split4h s1 = split4h(Racc[2 * kk + 1][nt] * kd1);
+                bh[kk][nt] = cat8h(s0.hi, s1.hi);
+                bl[kk][nt] = cat8h(s0.lo, s1.lo);
             }
         }
         // step t = (mt, kk) = (t / 2, t % 2): K^T rows d = 16 mt + li, tokens
         // 32 kk + 4 g4 + e and 32 kk + 16 + 4 g4 + e (the from-C order)
         auto kfrag = [&](int t) {
             const int mt = t >> 1, kk = t & 1;
-            const __bf16* kr = ktr + 32 * kk * SM::QLD + 16 * mt;
-            return cat8(ld4_tr(kr), ld4_tr(kr + 16 * SM::QLD));
+            const _Float16* kr = ktr + 32 * kk * SM::QLD + 16 * mt;
+            return cat8h(ld4_tr(kr), ld4_tr(kr + 16 * SM::QLD));
         };
         __builtin_amdgcn_sched_barrier(0);
         {
             constexpr int NSTEP = 2 * MT_S;
-            bf16x8 ka[3];
+            f16x8 ka[3];
             ka[0] = kfrag(0);
             ka[1] = kfrag(1);
 #pragma unroll
@@ -706,8 +739,8 @@ __global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs 
                 const int mt = t >> 1, kk = t & 1;
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    Sacc[mt][nt] = mma32(ka[t % 3], bh[kk][nt], Sacc[mt][nt]);
-                    Sacc[mt][nt] = mma32(ka[t % 3], bl[kk][nt], Sacc[mt][nt]);
+                    Sacc[mt][nt] = mma32h(ka[t % 3], bh[kk][nt], Sacc[mt][nt]);
+                    Sacc[mt][nt] = mma32h(ka[t % 3], bl[kk][nt], Sacc[mt][nt]);
                 }
             }
 #pragma unroll

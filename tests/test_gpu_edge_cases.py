@@ -11,7 +11,8 @@ Each expected value is the case's closed form, computed here in fp64 from the in
                                the key rows)   each token overwrites its key's row of
                                the state with v, so a query equal to a stored key
                                returns that token's v, and a query on an untouched row
-                               returns S_0's row -- every product is 0 or 1, so the
+                               returns S_0's row -- every product is 0 or 1, so with
+                               values exact in the 16-bit formats the kernels use the
                                GPU must give these values bitwise;
   full forgetting (g = -200)   e^g underflows to 0 in fp32: S_t = beta_t k_t v_t^T and
                                o_t = scale beta_t (k_t . q_t) v_t, whatever S_0 was.
@@ -79,11 +80,20 @@ def test_pure_decay_prefill(dtype, dk, dv, hk, hv):
                          atol, rtol)
 
 
+def _exact16(x):
+    """Values exact in bf16 and in fp16 alike (bf16 values of magnitude 2^-12 or more;
+    smaller ones are moved to +-2^-12), the formats the kernels feed matrix cores."""
+    x = W.round_to_bf16(np.asarray(x, dtype=np.float32))
+    tiny = np.abs(x) < 2.0 ** -12
+    x[tiny] = np.where(x[tiny] < 0, -(2.0 ** -12), 2.0 ** -12).astype(np.float32)
+    return x
+
+
 def _recall_workload(dtype, dk, dv, hk, hv, seed):
     """g = 0, beta = 1, scale 1; keys of each (sequence, key head) are distinct standard
     basis vectors on rows [0, n_keys); S_0 is zero on those rows and holds values
-    exact in the dtype on the rows above; each query is the key of an earlier token of
-    its sequence or one of the rows above."""
+    exact in every format on the rows above; each query is the key of an earlier token
+    of its sequence or one of the rows above."""
     reserve = 8
     n_keys = dk - reserve
     lengths = [n_keys, 1, n_keys - 23, 40, 0]
@@ -91,6 +101,7 @@ def _recall_workload(dtype, dk, dv, hk, hv, seed):
     w = W.make_workload("recall", seed=seed, H_k=hk, H_v=hv, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths,
                         num_slots=24, prefill_init="slots", start_pos=starts, export_grid=64, scale=1.0)
     rng = np.random.default_rng(seed + 1)
+    w.v[:] = _exact16(w.v)
     w.g[:] = 0.0
     w.beta[:] = 1.0
     w.q[:] = 0.0
@@ -107,8 +118,8 @@ def _recall_workload(dtype, dk, dv, hk, hv, seed):
                 r = perm[rng.integers(0, t + 1)] if rng.random() < 0.75 else n_keys + rng.integers(0, reserve)
                 w.q[a + t, kh, r] = 1.0
                 qrow[a + t, kh] = r
-    # S_0: zero on the key rows, values exact in bf16 (and fp32) on the rows above
-    s0 = W.round_to_bf16(rng.standard_normal(w.pool.shape, dtype=np.float32))
+    # S_0: zero on the key rows, values exact in every format on the rows above
+    s0 = _exact16(rng.standard_normal(w.pool.shape, dtype=np.float32))
     s0[:, :, :n_keys, :] = 0.0
     w.pool[:] = s0
     return w, n_keys, qrow

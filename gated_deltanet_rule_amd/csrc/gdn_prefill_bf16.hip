@@ -256,8 +256,15 @@ __device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
     j = t - i * (i + 1) / 2;
 }
 
+// Waves per SIMD the register allocation must allow: with one K buffer two workgroups
+// share a compute unit.
+template <int DV, int HG, int KB>
+constexpr int waves_per_simd() {
+    return (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 > 1 ? (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 : 1;
+}
+
 template <int DK, int DV, int HG, int KB>
-__global__ __launch_bounds__(HG * DV * 2, 3 - KB) void chunk_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void chunk_kernel(PrefillArgs a) {
     using SM = Smem<DK, DV, HG, KB>;
     constexpr int NWH = DV / 32;             // waves per value head
     constexpr int NW = HG * NWH;             // waves

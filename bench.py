@@ -59,8 +59,8 @@ def parse():
                          "dispatch of known traffic for hardware byte counters")
     ap.add_argument("--ingest-sq-counters", metavar="SQ_CSV",
                     help="no GPU work: turn the counter_collection.csv of a rocprofv3 --pmc run with "
-                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_* and SQ_WAVES into "
-                         "profiles/mfma_counters.json")
+                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_* (the bf16 and, if taken, the fp16 "
+                         "MFMA op counts) and SQ_WAVES into profiles/mfma_counters.json")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the counter_collection.csv files of a rocprofv3 --pmc FETCH_SIZE "
                          "run and a --pmc WRITE_SIZE run of this bench into profiles/hbm_traffic.json")
@@ -156,6 +156,8 @@ def ingest_sq_counters(sq_csv, chunks_per_wave=128):
                "lds_insts_per_unit": round(mean("SQ_INSTS_LDS") / units, 1),
                "unit": "wave and chunk" if kernel == "chunk_kernel" else "wave",
                "executed_bf16_mfma_flop": mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512}
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in next(iter(disp.values())):
+            rec["executed_f16_mfma_flop"] = mean("SQ_INSTS_VALU_MFMA_MOPS_F16") * 512
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in next(iter(disp.values())):
             busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
             rec["valu_coexec_frac_of_mfma_busy"] = round(mean("SQ_VALU_MFMA_COEXEC_CYCLES") / busy, 4) if busy else None

@@ -41,7 +41,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 CHUNK = 64
-KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "chunk_kernel": "gdn_prefill_bf16.hip"}
+KERNEL_SOURCES = {"decode_kernel": "gdn_decode.hip", "chunk_kernel": "gdn_prefill_bf16.hip",
+                  "stream_copy_kernel": "gdn_probe.hip", "state_rmw_kernel": "gdn_probe.hip"}
 
 
 def parse():
@@ -436,6 +437,7 @@ def main():
     st_pre = stats([e[1].elapsed_time(e[2]) for e in ev])
     t_pre_b2b = time_loop(torch, stage_prefill, K)
     t_dec_b2b = decode_back_to_back(torch, binding, wd, dq, dk_, dv_, dg, db, do, pool, dev)
+    t_copy_ref, t_rmw_ref = decode_floors(torch, wd, pool, dev)
     t_dec, t_pre = st_dec["median"], st_pre["median"]
 
     # ---- figures
@@ -482,7 +484,15 @@ def main():
                    # 256-slot cache (every launch's states cold), without a pair of events
                    # around each launch
                    "back_to_back_ms": round(t_dec_b2b, 5),
-                   "back_to_back_frac_of_hbm_peak": round(dec_bytes / (t_dec_b2b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+                   "back_to_back_frac_of_hbm_peak": round(dec_bytes / (t_dec_b2b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   # the same bytes in two reference patterns, timed the same way: a plain
+                   # streaming copy, and the decode's read-reduce-write dependency
+                   # without its arithmetic (libgdn_probe.so)
+                   "stream_copy_ms": round(t_copy_ref, 5),
+                   "stream_copy_frac_of_hbm_peak": round(dec_bytes / (t_copy_ref * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "state_rmw_ms": round(t_rmw_ref, 5),
+                   "state_rmw_frac_of_hbm_peak": round(dec_bytes / (t_rmw_ref * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "back_to_back_frac_of_state_rmw": round(t_rmw_ref / t_dec_b2b, 4)},
         "prefill": {"tokens_per_s": round(Tp / (t_pre * 1e-3), 1), "ms": t_pre,
                     "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                     "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "flops_per_token": f_tok,
@@ -521,6 +531,53 @@ def decode_back_to_back(torch, binding, wd, q, k, v, g, beta, o, pool, dev, roun
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (rounds * nsets)
+
+
+def probe_library():
+    """libgdn_probe.so: the memory-pattern reference kernels (a streaming copy and the
+    decode's read-reduce-write pattern without its arithmetic)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_rule_amd", "libgdn_probe.so"))
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.gdn_probe_stream_copy.restype = i32
+    lib.gdn_probe_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.gdn_probe_state_rmw.restype = i32
+    lib.gdn_probe_state_rmw.argtypes = [vp, i32, i32, vp, i32, vp]
+    return lib
+
+
+def decode_floors(torch, wd, pool, dev, rounds=5):
+    """What HBM delivers for the decode batch's bytes (2 x 128 MiB of state per launch)
+    in two reference patterns, each timed back to back like the decode: a streaming
+    copy of 128 MiB rotating over 4 disjoint source/destination pairs of a 1 GiB
+    buffer, and the decode's read-reduce-write pattern without its arithmetic over the
+    same 4 disjoint 64-slot sets of the cache.  Returns (copy ms, rmw ms)."""
+    import ctypes
+    lib = probe_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    B, H_v = wd.num_decode_rows, wd.H_v
+    nbytes = 4 * wd.d_k * wd.d_v * B * H_v
+    buf = torch.empty(8 * nbytes // 4, dtype=torch.float32, device=dev)
+    pairs = [(buf.data_ptr() + i * nbytes, buf.data_ptr() + (i + 4) * nbytes) for i in range(4)]
+    slots = wd.pool.shape[0]
+    perm = np.concatenate([wd.slot_in, np.setdiff1d(np.arange(slots), wd.slot_in)]).astype(np.int32)
+    sets = [torch.as_tensor(perm[i * B:(i + 1) * B], device=dev) for i in range(slots // B)]
+
+    def copy():
+        for sp, dp in pairs:
+            assert lib.gdn_probe_stream_copy(ctypes.c_void_p(sp), ctypes.c_void_p(dp), nbytes, stream) == 0
+
+    def rmw():
+        for st in sets:
+            assert lib.gdn_probe_state_rmw(ctypes.c_void_p(pool.data_ptr()), pool.shape[0], H_v,
+                                           ctypes.c_void_p(st.data_ptr()), B, stream) == 0
+
+    copy()
+    rmw()
+    t_copy = time_loop(torch, copy, rounds) / len(pairs)
+    t_rmw = time_loop(torch, rmw, rounds) / len(sets)
+    del buf
+    return t_copy, t_rmw
 
 
 def copy_bandwidth(torch, dev, mib=1024, reps=10):

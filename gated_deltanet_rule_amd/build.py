@@ -1,4 +1,5 @@
-"""Build libgdn.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc."""
+"""Build libgdn.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc, and
+libgdn_probe.so (the benchmark's memory-pattern reference kernels)."""
 from __future__ import annotations
 
 import os
@@ -12,6 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_prefill_bf16.hip"]
+PROBE_LIB = os.path.join(HERE, "libgdn_probe.so")
+PROBE_SOURCES = ["gdn_probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ALU ops are switched off for every device pass (the hipcc host pass
@@ -44,14 +47,18 @@ def build(verbose: bool = False) -> str:
             print(out, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("link failed:\n%s" % (res.stdout + res.stderr))
-    os.replace(tmp, LIB)
+    def link(objs, out):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n%s" % (res.stdout + res.stderr))
+        os.replace(tmp, out)
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

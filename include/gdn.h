@@ -49,6 +49,10 @@
  *               row's output and state are bitwise identical whatever the batch
  *               size, its position in the batch, or the prefills sharing its step;
  *               a prefill sequence's results do not depend on its batch-mates.
+ *   Range       bf16 prefills feed the matrix cores fp16 operands for q, k, the
+ *               state and the per-token updates: q and k are expected L2-normalised
+ *               (as the rule uses them), and states, values and outputs must stay
+ *               below 2^15 in magnitude.  fp32 inputs and decode have no such limit.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -141,7 +145,8 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows,
  *   start_pos  device [num_seqs] int32 or NULL (= all 0): absolute position of each
  *              sequence's first token, >= 0 (a negative value is outside the contract:
  *              the device cannot be checked without a sync).  Chunks lie on the absolute
- *              64-token grid: a sequence starting off the grid begins with a short chunk.
+ *              64-token grid: a sequence starting off the grid begins with a short chunk,
+ *              and one ending off the grid ends with one.
  *   export_grid 0 = no export.  Otherwise a positive multiple of 64 (for example 64,
  *              or 1088 = lcm(64, 1088)); the state after every absolute position p with
  *              p % export_grid == 0 and start_pos < p <= start_pos + length is written
@@ -165,8 +170,20 @@ gdn_status gdn_recurrent_decode(const gdn_shape* shape, int32_t num_rows,
  *   workspace  device scratch of at least gdn_chunk_prefill_workspace_size() bytes,
  *              256-byte aligned, contents need no initialisation; may be NULL when
  *              that size is 0.
- *   num_seqs == 0 or total_tokens == 0 is a no-op returning GDN_OK (a zero-length
- *   sequence inside a batch copies its initial state to its final slot).
+ *   num_seqs == 0 is a no-op returning GDN_OK.  A zero-length sequence copies its
+ *   initial state (zeros without one) to its final slot; with total_tokens == 0 every
+ *   sequence is empty and does just that.
+ *
+ *   Splitting a prompt across calls.  A resume at an absolute position that is a
+ *   multiple of 64, from the state exported there, continues with the unsplit run's
+ *   arithmetic, so its outputs and final state are bitwise those of the unsplit run.
+ *   A split at any other token t is made bitwise the same way: a partial last chunk
+ *   gives its rows the bits the full chunk would (within a chunk a row combines only
+ *   rows at or before it), so the call that ends at t returns the unsplit run's
+ *   outputs up to t; the next call starts at t0 = 64 floor(t / 64) from the state
+ *   after t0 (an export on a 64 grid, or the initial state when no grid point was
+ *   crossed) and re-feeds the t - t0 < 64 tokens since, whose outputs come out
+ *   bitwise equal again and may be discarded.
  */
 gdn_status gdn_chunk_prefill(const gdn_shape* shape, int32_t num_seqs, int64_t total_tokens,
                              const int32_t* cu_seqlens, const void* q, const void* k,

@@ -74,12 +74,14 @@ def product(fa, a, fb, b):
 
 def chain(q, k, v, g, beta, scale, S0, scheme=KERNEL, **override):
     """One chain: q, k [T, d_k]; v [T, d_v]; g, beta [T]; S0 [d_k, d_v].  Returns
-    (o [T, d_v] rounded to bf16, final state [d_k, d_v]).  ``override`` replaces
-    single entries of the scheme."""
+    (o [T, d_v] rounded to bf16, the states after each chunk [ceil(T / 64), d_k,
+    d_v]; the last one is the final state).  ``override`` replaces single entries of
+    the scheme."""
     f = dict(scheme, **override)
     T = q.shape[0]
     S = np.array(S0, dtype=np.float64)
     o = np.zeros((T, v.shape[1]))
+    states = []
     q = _round(f["qk"], q)
     k = _round(f["qk"], k)
     for c0 in range(0, T, C):
@@ -105,4 +107,5 @@ def chain(q, k, v, g, beta, scale, S0, scheme=KERNEL, **override):
         o[c0:c0 + L] = bf16(scale * gam[:, None] * (Q @ Ss) + PU)
         dU = np.exp(G[-1] - G)[:, None] * U
         S = gam[-1] * S + product("exact", K.T, f["upd_u"], dU)
-    return o, S
+        states.append(S)
+    return o, np.array(states)

@@ -44,13 +44,13 @@
 // formats.  q and k are staged in LDS as fp16 (exact for the normalised keys and
 // queries of the rule, down to 2^-24 below fp16's normal range), and every product
 // with Q, K or K^T is an fp16 one: K K^T, Q K^T, Z = K S and Q S with S rounded once
-// to fp16, and the state update with the decayed U as an fp16 hi + lo pair.  The
-// output product takes P and U as single fp16 values, and so does T_ii X_i.  The
-// off-diagonal solve products -A_ij U_j take both sides as bf16 hi + lo pairs (x =
-// hi + lo to about 2^-17) in three products, and V enters exactly through a bf16
-// identity product.  fp16 has four times bf16's precision, which is what lets single
-// roundings stand where bf16 needed pairs; its range bounds the values: states,
-// values and outputs must stay below 2^15 in magnitude.  Gates, the A_ii inverses
+// to fp16, and the state update with the decayed U as an fp16 hi + lo pair (x = hi +
+// lo to about 2^-22).  The off-diagonal solve products -A_ij U_j take both sides as
+// fp16 pairs, in three products.  The output product takes P and U as single fp16
+// values, and so does T_ii X_i.  V enters exactly through a bf16 identity product.
+// fp16 has four times bf16's precision, which is what lets single roundings stand
+// where bf16 would need pairs; its range bounds the values: states, values and
+// outputs must stay below 2^15 in magnitude.  Gates, the A_ii inverses
 // and all accumulators are fp32.  A sequence's work never depends on the other
 // sequences of the call, so its results are bitwise independent of its batch-mates;
 // chunks lie on the absolute 64-token grid, so a resume from an exported grid state
@@ -70,11 +70,11 @@ using dev::kC;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- MFMA operands
 //
@@ -85,9 +85,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // lane.  16x16x16: lane group g holds k = 4g..4g+3, which is exactly the rows one C
 // tile holds, so a C tile converted to bf16 is a B operand as it stands.
 
-__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
                                                      c, 0, 0, 0);
@@ -97,44 +94,6 @@ __device__ __forceinline__ f32x4 mma32h(f16x8 a, f16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mma16h(f16x4 a, f16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-struct Split4 { bf16x4 hi, lo; };
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// x = hi + lo: hi rounded to bf16, lo the exact remainder rounded once (two values
-// per conversion instruction).  The remainder x - hi comes from one bf16 dot product
-// per value, hi . (-1, 0) + x or hi . (0, -1) + x, which is exact (the true result is
-// representable) and saves widening hi back to fp32 first.  The two packed (-1, 0)
-// constants are made in SGPRs: left to the compiler they become inline constants,
-// and those did not read as the intended bf16 pairs.
-__device__ __forceinline__ Split4 split4(f32x4 x) {
-    const f32x2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
-    const bf16x2 h01 = __builtin_convertvector(x01, bf16x2);
-    const bf16x2 h23 = __builtin_convertvector(x23, bf16x2);
-    unsigned c0, c1;
-    asm("s_mov_b32 %0, 0xbf80" : "=s"(c0));       // bf16 pair (-1, 0)
-    asm("s_mov_b32 %0, 0xbf800000" : "=s"(c1));   // bf16 pair (0, -1)
-    const bf16x2 m0 = __builtin_bit_cast(bf16x2, c0), m1 = __builtin_bit_cast(bf16x2, c1);
-    const f32x2 r01 = {__builtin_amdgcn_fdot2_f32_bf16(h01, m0, x[0], false),
-                       __builtin_amdgcn_fdot2_f32_bf16(h01, m1, x[1], false)};
-    const f32x2 r23 = {__builtin_amdgcn_fdot2_f32_bf16(h23, m0, x[2], false),
-                       __builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false)};
-    const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
-    const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
-    Split4 s;
-    s.hi = bf16x4{h01[0], h01[1], h23[0], h23[1]};
-    s.lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
-    return s;
-}
-
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    bf16x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return r;
 }
 
 // fp16 values are moved as whole 32-bit words (bit casts of packed pairs), never as
@@ -152,25 +111,36 @@ __device__ __forceinline__ f16x4 cvt4h(f32x4 x) {
     return __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)));
 }
 
-struct Split4h { f16x4 hi, lo; };
+// The remainder x - h of an fp32 value and an fp16 value held in the low (or high)
+// half of a packed pair: one mixed-precision FMA, h (-1) + x, which is exact (the
+// true result is representable) and saves widening h to fp32 first.  Probed on
+// gfx950 against widening and subtracting: bitwise equal for magnitudes 2^-34 to
+// 2^15, fp16 subnormals included.
+__device__ __forceinline__ float rem_lo(unsigned hpair, float x) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpair), "v"(x));
+    return r;
+}
+__device__ __forceinline__ float rem_hi(unsigned hpair, float x) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpair), "v"(x));
+    return r;
+}
 
-// x = hi + lo in fp16: hi rounded, lo the remainder x - hi (from one fp16 dot product
-// per value, exact while hi is a normal fp16) rounded once; x = hi + lo to about
-// 2^-22.  The (-1, 0) pairs are made in SGPRs, as for the bf16 split.
+// The lo part of x = hi + lo in fp16, given hi = x rounded to fp16: the remainder
+// rounded once; x = hi + lo to about 2^-22.
+__device__ __forceinline__ f16x4 lo4h(f32x4 x, f16x4 hi) {
+    const uint2 w = __builtin_bit_cast(uint2, hi);
+    const f16x2 a = __builtin_convertvector((f32x2{rem_lo(w.x, x[0]), rem_hi(w.x, x[1])}), f16x2);
+    const f16x2 b = __builtin_convertvector((f32x2{rem_lo(w.y, x[2]), rem_hi(w.y, x[3])}), f16x2);
+    return __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)));
+}
+
+struct Split4h { f16x4 hi, lo; };
 __device__ __forceinline__ Split4h split4h(f32x4 x) {
-    const f16x2 h01 = __builtin_convertvector((f32x2{x[0], x[1]}), f16x2);
-    const f16x2 h23 = __builtin_convertvector((f32x2{x[2], x[3]}), f16x2);
-    unsigned c0, c1;
-    asm("s_mov_b32 %0, 0xbc00" : "=s"(c0));       // fp16 pair (-1, 0)
-    asm("s_mov_b32 %0, 0xbc000000" : "=s"(c1));   // fp16 pair (0, -1)
-    const f16x2 m0 = __builtin_bit_cast(f16x2, c0), m1 = __builtin_bit_cast(f16x2, c1);
-    const f32x2 r01 = {__builtin_amdgcn_fdot2(h01, m0, x[0], false), __builtin_amdgcn_fdot2(h01, m1, x[1], false)};
-    const f32x2 r23 = {__builtin_amdgcn_fdot2(h23, m0, x[2], false), __builtin_amdgcn_fdot2(h23, m1, x[3], false)};
-    const f16x2 l01 = __builtin_convertvector(r01, f16x2);
-    const f16x2 l23 = __builtin_convertvector(r23, f16x2);
     Split4h s;
-    s.hi = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, h01), __builtin_bit_cast(unsigned, h23)));
-    s.lo = __builtin_bit_cast(f16x4, make_uint2(__builtin_bit_cast(unsigned, l01), __builtin_bit_cast(unsigned, l23)));
+    s.hi = cvt4h(x);
+    s.lo = lo4h(x, s.hi);
     return s;
 }
 
@@ -183,8 +153,6 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w) {
     return make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w));
 }
 
-__device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-__device__ __forceinline__ void st4(__bf16* p, bf16x4 x) { *reinterpret_cast<bf16x4*>(p) = x; }
 __device__ __forceinline__ f16x4 ld4h(const _Float16* p) { return *reinterpret_cast<const f16x4*>(p); }
 __device__ __forceinline__ f16x8 ld8h(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ void st4h(_Float16* p, f16x4 x) { *reinterpret_cast<f16x4*>(p) = x; }
@@ -242,8 +210,8 @@ struct Smem {
                                               // chunk c reads it while chunk c+1 is
                                               // staged); one: staged after the update
     struct Head {
-        __bf16 sol[10][2][BSZ];               // block (i, j): -A_ij (j < i), bf16 hi, lo; or
-                                              // T_ii, fp16, in the hi slot
+        _Float16 sol[10][2][BSZ];             // block (i, j): -A_ij (j < i) as an fp16 hi,
+                                              // lo pair; or T_ii, fp16, in the hi slot
         _Float16 p[10][BSZ];                  // P blocks (fp16)
         float at[4 * ATB];                    // A_ii^T: at[b * ATB + s * ATLD + r] = A_bb[r][s]
         float gate[2][kGates * kC];           // by chunk parity
@@ -563,9 +531,9 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                         const float fr = gx[GATE_FS * kC + r] * __builtin_amdgcn_exp2f(c2);
                         const f32x4 te = *reinterpret_cast<const f32x4*>(gx + GATE_TE * kC + s0);
                         if (tt < 6) {            // -A_ij = -beta_r (K K^T)_rs D_rs
-                            const Split4 sp = split4(acc * te * -(fr * gx[GATE_BET * kC + r]));
-                            st4(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
-                            st4(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                            const Split4h sp = split4h(acc * te * -(fr * gx[GATE_BET * kC + r]));
+                            st4h(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                            st4h(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
                         } else {
                             st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(acc * te * (a.scale * fr)));
                         }
@@ -638,45 +606,46 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
-        Split4 Us[4][2];                     // U blocks as bf16 pairs (the solve)
-        f16x4 Uh[4][2];                      // and as single fp16 values (the output product)
+        f16x4 Uh[4][2], Ul[4][2];             // U blocks as fp16 hi + lo pairs; hi alone in
+                                              // the output product
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 // blocks j in pairs on 16x16x32 (the pair's U registers side by side are
-                // the from-C operand); a last odd block on 16x16x32 too, with A's hi and
-                // lo side by side against U's hi twice, then against U's lo twice (the
-                // lo lo term comes free).  Every product that accumulates into X has one shape:
-                // back-to-back dependent MFMAs pass the accumulator on without wait
-                // states only between identical instructions, and the compiler does not
-                // pad a 16x16x32 -> 16x16x16 switch on the same registers.
+                // the from-C operand), three products: A hi U hi, A hi U lo, A lo U hi; a
+                // last odd block on 16x16x32 too, with A's hi and lo side by side against
+                // U's hi twice, then against U's lo twice (the lo lo term comes free).
+                // Every product that accumulates into X has one shape: back-to-back
+                // dependent MFMAs pass the accumulator on without wait states only
+                // between identical instructions, and the compiler does not pad a
+                // 16x16x32 -> 16x16x16 switch on the same registers.
                 f32x4 X = Racc[i][nt];
 #pragma unroll
                 for (int j = 0; j + 1 < i; j += 2) {
-                    const bf16x8 ah = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
-                                           ld4(hd.sol[blk(i, j + 1)][0] + li * SM::BLD + 4 * g4));
-                    const bf16x8 al = cat8(ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4),
-                                           ld4(hd.sol[blk(i, j + 1)][1] + li * SM::BLD + 4 * g4));
-                    const bf16x8 uh = cat8(Us[j][nt].hi, Us[j + 1][nt].hi);
-                    const bf16x8 ul = cat8(Us[j][nt].lo, Us[j + 1][nt].lo);
-                    X = mma32(ah, uh, X);
-                    X = mma32(ah, ul, X);
-                    X = mma32(al, uh, X);
+                    const f16x8 ah = cat8h(ld4h(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
+                                           ld4h(hd.sol[blk(i, j + 1)][0] + li * SM::BLD + 4 * g4));
+                    const f16x8 al = cat8h(ld4h(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4),
+                                           ld4h(hd.sol[blk(i, j + 1)][1] + li * SM::BLD + 4 * g4));
+                    const f16x8 uh = cat8h(Uh[j][nt], Uh[j + 1][nt]);
+                    const f16x8 ul = cat8h(Ul[j][nt], Ul[j + 1][nt]);
+                    X = mma32h(ah, uh, X);
+                    X = mma32h(ah, ul, X);
+                    X = mma32h(al, uh, X);
                 }
                 if (i & 1) {
                     const int j = i - 1;
-                    const bf16x8 a2 = cat8(ld4(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
-                                           ld4(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4));
-                    X = mma32(a2, cat8(Us[j][nt].hi, Us[j][nt].hi), X);
-                    X = mma32(a2, cat8(Us[j][nt].lo, Us[j][nt].lo), X);
+                    const f16x8 a2 = cat8h(ld4h(hd.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4),
+                                           ld4h(hd.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4));
+                    X = mma32h(a2, cat8h(Uh[j][nt], Uh[j][nt]), X);
+                    X = mma32h(a2, cat8h(Ul[j][nt], Ul[j][nt]), X);
                 }
                 // U_i = T_ii X_i, both single fp16 values
-                const f16x4 th = ld4h(reinterpret_cast<const _Float16*>(hd.sol[blk(i, i)][0]) + li * SM::BLD + 4 * g4);
+                const f16x4 th = ld4h(hd.sol[blk(i, i)][0] + li * SM::BLD + 4 * g4);
                 const f32x4 U = mma16h(th, cvt4h(X), f32x4{0.f, 0.f, 0.f, 0.f});
                 Racc[i][nt] = U;
-                Us[i][nt] = split4(U);
                 Uh[i][nt] = cvt4h(U);
+                Ul[i][nt] = lo4h(U, Uh[i][nt]);
             }
             // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, U and P as
             // single fp16 values, blocks in pairs on 16x16x32 products; a last single

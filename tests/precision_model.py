@@ -18,7 +18,7 @@ is finer than the kernel's fp32 and does not change what the model is for: showi
 which roundings a bound can or cannot absorb.
 
 KERNEL is the kernel's scheme: q and k in fp16; S once to fp16 in K S and Q S; -A_ij
-and U as bf16 pairs in the solve; T_ii and the right-hand side single fp16; P and U
+and U as fp16 pairs in the solve; T_ii and the right-hand side single fp16; P and U
 single fp16 in the output product; the decayed U as an fp16 pair in the state
 update.  EARLIER is the previous all-bf16 scheme (S once to bf16, every other operand
 a bf16 pair), kept for comparison.
@@ -32,7 +32,7 @@ from gated_deltanet_rule_amd.workloads import round_to_bf16
 C = 64
 BLOCK = 16
 
-KERNEL = dict(qk="f16", s="f16", solve_a="bf16x2", solve_u="bf16x2", tii="f16", rhs="f16", out_p="f16",
+KERNEL = dict(qk="f16", s="f16", solve_a="f16x2", solve_u="f16x2", tii="f16", rhs="f16", out_p="f16",
               out_u="f16", upd_u="f16x2")
 EARLIER = dict(qk="exact", s="bf16", solve_a="bf16x2", solve_u="bf16x2", tii="bf16x2", rhs="bf16x2",
                out_p="bf16x2", out_u="bf16x2", upd_u="bf16x2")

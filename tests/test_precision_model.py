@@ -79,7 +79,7 @@ def test_kernel_scheme_is_no_worse_than_the_all_bf16_one():
 
 @pytest.mark.parametrize("name", ["no decay, d 128", "no decay, d_k 64, d_v 128"])
 def test_single_fp16_solve_products_exceed_the_bound(name):
-    """The off-diagonal solve products -A_ij U_j keep bf16 pairs: with single fp16
+    """The off-diagonal solve products -A_ij U_j keep fp16 pairs: with single fp16
     values on both sides the states leave the bound."""
     _, s = _worst_ratio(*CASES[name], solve_a="f16", solve_u="f16")
     assert s > 1.0, (name, s)

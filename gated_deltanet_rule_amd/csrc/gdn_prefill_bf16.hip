@@ -167,23 +167,23 @@ __device__ __forceinline__ f16x4 ld4_tr(const _Float16* p) {
     return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
-// A lane offset the compiler cannot relate to the one it came from.  Two 8-byte LDS
-// reads whose addresses differ by a known constant are paired by the compiler into one
-// ds_read2_b64, and on gfx950 that instruction took four times as long as the two
-// single reads for the same bytes (16 cycles per wave and kilobyte against 4 to 8, in
-// a probe that reads the Q/K row fragments below).  Reads through a second base
-// register stay single.
-__device__ __forceinline__ int apart(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
+// An 8-byte LDS read the compiler keeps single.  Two 8-byte LDS reads whose addresses
+// differ by a known constant are otherwise paired into one ds_read2_b64, and on gfx950
+// that instruction took four times as long as the two single reads of the same bytes
+// (16 cycles per wave and kilobyte against 4 to 8, in a probe that reads the Q/K row
+// fragments below).  A volatile read is never paired.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) volatile u32x2 lds_vu32x2;
+__device__ __forceinline__ f16x4 ld4h_single(const _Float16* p) {
+    const u32x2 w = *(lds_vu32x2*)(p);
+    return __builtin_bit_cast(f16x4, w);
 }
 
-// 16x32 operand of a row-major Q or K row in LDS, k from 32 ks in from-C order: the
-// lane's two 8-byte pieces at column offsets o[0] = (4 g) ^ sw + 32 ks and o[1] = o[0] +
-// 16 (sw the row's swizzle, see Smem; it only touches column bit 3), each offset
-// apart() from every other.
-__device__ __forceinline__ f16x8 row_fromc(const _Float16* row, const int (&o)[2]) {
-    return cat8h(ld4h(row + o[0]), ld4h(row + o[1]));
+// 16x32 operand of a row-major Q or K row in LDS, k from 32 ks in from-C order; sw is
+// the row's column swizzle (see Smem; it only touches column bit 3)
+__device__ __forceinline__ f16x8 row_fromc(const _Float16* row, int ks, int g, int sw) {
+    const _Float16* p = row + ((4 * g) ^ sw);
+    return cat8h(ld4h_single(p + 32 * ks), ld4h_single(p + 32 * ks + 16));
 }
 
 // B operand (from-C order, k step ks) out of a pair of state accumulator tiles, in fp16
@@ -568,11 +568,6 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         const float* gt = hd.gate[buf];
         f32x4 Racc[4][2], Oacc[4][2];
         {
-            int zo[KS_DK][2];                 // every piece through its own base register
-#pragma unroll
-            for (int kk = 0; kk < KS_DK; ++kk)
-#pragma unroll
-                for (int pc = 0; pc < 2; ++pc) zo[kk][pc] = apart(((4 * g4) ^ (li & 8)) + 32 * kk + 16 * pc);
             f16x8 Sb[KS_DK][2];
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk)
@@ -583,8 +578,8 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    const f16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, zo[kk]);
-                    const f16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, zo[kk]);
+                    const f16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
+                    const f16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         Racc[mt][nt] = mma32h(ak, Sb[kk][nt], Racc[mt][nt]);
@@ -623,8 +618,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
-        // the lane's offset in a 16x16 block, and a copy for the second block of a pair
-        const int bo = li * SM::BLD + 4 * g4, bo1 = apart(bo);
+        const int bo = li * SM::BLD + 4 * g4;   // the lane's offset in a 16x16 block
         f16x4 Uh[4][2], Ul[4][2];             // U blocks as fp16 hi + lo pairs; hi alone in
                                               // the output product
 #pragma unroll
@@ -642,8 +636,8 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 f32x4 X = Racc[i][nt];
 #pragma unroll
                 for (int j = 0; j + 1 < i; j += 2) {
-                    const f16x8 ah = cat8h(ld4h(hd.sol[blk(i, j)][0] + bo), ld4h(hd.sol[blk(i, j + 1)][0] + bo1));
-                    const f16x8 al = cat8h(ld4h(hd.sol[blk(i, j)][1] + bo), ld4h(hd.sol[blk(i, j + 1)][1] + bo1));
+                    const f16x8 ah = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j + 1)][0] + bo));
+                    const f16x8 al = cat8h(ld4h_single(hd.sol[blk(i, j)][1] + bo), ld4h_single(hd.sol[blk(i, j + 1)][1] + bo));
                     const f16x8 uh = cat8h(Uh[j][nt], Uh[j + 1][nt]);
                     const f16x8 ul = cat8h(Ul[j][nt], Ul[j + 1][nt]);
                     X = mma32h(ah, uh, X);
@@ -652,12 +646,12 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 }
                 if (i & 1) {
                     const int j = i - 1;
-                    const f16x8 a2 = cat8h(ld4h(hd.sol[blk(i, j)][0] + bo), ld4h(hd.sol[blk(i, j)][1] + bo1));
+                    const f16x8 a2 = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j)][1] + bo));
                     X = mma32h(a2, cat8h(Uh[j][nt], Uh[j][nt]), X);
                     X = mma32h(a2, cat8h(Ul[j][nt], Ul[j][nt]), X);
                 }
                 // U_i = T_ii X_i, both single fp16 values
-                const f16x4 th = ld4h(hd.sol[blk(i, i)][0] + bo);
+                const f16x4 th = ld4h_single(hd.sol[blk(i, i)][0] + bo);
                 const f32x4 U = mma16h(th, cvt4h(X), f32x4{0.f, 0.f, 0.f, 0.f});
                 Racc[i][nt] = U;
                 Uh[i][nt] = cvt4h(U);
@@ -671,8 +665,8 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
             for (int kk = 0; 2 * kk <= i; ++kk) {
                 const int j0 = 2 * kk, j1 = 2 * kk + 1;
-                const f16x4 p0 = ld4h(hd.p[blk(i, j0)] + bo);
-                const f16x8 pp = cat8h(p0, j1 <= i ? ld4h(hd.p[blk(i, j1)] + bo1) : zero4);
+                const f16x4 p0 = ld4h_single(hd.p[blk(i, j0)] + bo);
+                const f16x8 pp = cat8h(p0, j1 <= i ? ld4h_single(hd.p[blk(i, j1)] + bo) : zero4);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     Oacc[i][nt] = mma32h(cat8h(Uh[j0][nt], Uh[j1 <= i ? j1 : j0][nt]), pp, Oacc[i][nt]);

@@ -508,7 +508,11 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
             }
         } else {
             constexpr int NTI = (16 + NNL - 1) / NNL;
-            const int nl = hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);   // index among the others
+            // index among the others.  Waves wv and wv ^ 4 share a SIMD (probed); with two
+            // heads of four waves the first waves are 0 and 5, and their SIMD partners 4
+            // and 1 take the two slots with two tiles, the other four waves three each.
+            const int nl = NW == 8 ? (int)((0x32051040u >> (4 * wv)) & 15u)
+                                   : hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);
 #pragma unroll
             for (int n = 0; n < NTI; ++n) {
                 const int tt = nl + NNL * n;     // wave-uniform: 0..5 K K^T, 6..15 Q K^T

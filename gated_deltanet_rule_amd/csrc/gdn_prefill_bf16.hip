@@ -625,41 +625,47 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         const int bo = li * SM::BLD + 4 * g4;   // the lane's offset in a 16x16 block
         f16x4 Uh[4][2], Ul[4][2];             // U blocks as fp16 hi + lo pairs; hi alone in
                                               // the output product
+        // X_i = R_i - sum_{j<i} A_ij U_j accumulates in Racc[i] as soon as each U_j exists
+        // (right-looking), so that only one block product lies between U_i and
+        // X_(i+1): block (i, j) alone on 16x16x32, A's hi and lo side by side against
+        // U's hi twice, then against U's lo twice (the lo lo term comes free); blocks
+        // (0, 1) of row 3 as a pair, three products (A hi U hi, A hi U lo, A lo U hi),
+        // off that chain.  Every product that accumulates into X has one shape:
+        // back-to-back dependent MFMAs pass the accumulator on without wait states only
+        // between identical instructions, and the compiler does not pad a 16x16x32 ->
+        // 16x16x16 switch on the same registers.
+        auto upd1 = [&](int i, int j) __attribute__((always_inline)) {
+            const f16x8 a2 = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j)][1] + bo));
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                Racc[i][nt] = mma32h(a2, cat8h(Uh[j][nt], Uh[j][nt]), Racc[i][nt]);
+                Racc[i][nt] = mma32h(a2, cat8h(Ul[j][nt], Ul[j][nt]), Racc[i][nt]);
+            }
+        };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                // blocks j in pairs on 16x16x32 (the pair's U registers side by side are
-                // the from-C operand), three products: A hi U hi, A hi U lo, A lo U hi; a
-                // last odd block on 16x16x32 too, with A's hi and lo side by side against
-                // U's hi twice, then against U's lo twice (the lo lo term comes free).
-                // Every product that accumulates into X has one shape: back-to-back
-                // dependent MFMAs pass the accumulator on without wait states only
-                // between identical instructions, and the compiler does not pad a
-                // 16x16x32 -> 16x16x16 switch on the same registers.
-                f32x4 X = Racc[i][nt];
-#pragma unroll
-                for (int j = 0; j + 1 < i; j += 2) {
-                    const f16x8 ah = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j + 1)][0] + bo));
-                    const f16x8 al = cat8h(ld4h_single(hd.sol[blk(i, j)][1] + bo), ld4h_single(hd.sol[blk(i, j + 1)][1] + bo));
-                    const f16x8 uh = cat8h(Uh[j][nt], Uh[j + 1][nt]);
-                    const f16x8 ul = cat8h(Ul[j][nt], Ul[j + 1][nt]);
-                    X = mma32h(ah, uh, X);
-                    X = mma32h(ah, ul, X);
-                    X = mma32h(al, uh, X);
-                }
-                if (i & 1) {
-                    const int j = i - 1;
-                    const f16x8 a2 = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j)][1] + bo));
-                    X = mma32h(a2, cat8h(Uh[j][nt], Uh[j][nt]), X);
-                    X = mma32h(a2, cat8h(Ul[j][nt], Ul[j][nt]), X);
-                }
                 // U_i = T_ii X_i, both single fp16 values
                 const f16x4 th = ld4h_single(hd.sol[blk(i, i)][0] + bo);
-                const f32x4 U = mma16h(th, cvt4h(X), f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 U = mma16h(th, cvt4h(Racc[i][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
                 Racc[i][nt] = U;
                 Uh[i][nt] = cvt4h(U);
                 Ul[i][nt] = lo4h(U, Uh[i][nt]);
+            }
+            if (i + 1 < 4) upd1(i + 1, i);    // the next block's last product: on the chain
+            if (i == 0) upd1(2, 0);
+            if (i == 1) {                     // blocks (0, 1) of row 3 as a pair
+                const f16x8 ah = cat8h(ld4h_single(hd.sol[blk(3, 0)][0] + bo), ld4h_single(hd.sol[blk(3, 1)][0] + bo));
+                const f16x8 al = cat8h(ld4h_single(hd.sol[blk(3, 0)][1] + bo), ld4h_single(hd.sol[blk(3, 1)][1] + bo));
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const f16x8 uh = cat8h(Uh[0][nt], Uh[1][nt]);
+                    const f16x8 ul = cat8h(Ul[0][nt], Ul[1][nt]);
+                    Racc[3][nt] = mma32h(ah, uh, Racc[3][nt]);
+                    Racc[3][nt] = mma32h(ah, ul, Racc[3][nt]);
+                    Racc[3][nt] = mma32h(al, uh, Racc[3][nt]);
+                }
             }
             // O rows 16 i .. 16 i + 15, transposed: + U_(0..i)^T P_i,(0..i)^T, U and P as
             // single fp16 values, blocks in pairs on 16x16x32 products; a last single

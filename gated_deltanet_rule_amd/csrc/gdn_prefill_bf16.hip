@@ -252,9 +252,15 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
     constexpr int KS_DK = DK / 32;           // 32-wide k steps over d_k
     constexpr int VPR = DK / 8;              // 16-byte vectors per Q/K row
-    constexpr int NQ = kC * VPR / NT;        // prefetched Q (and K) vectors per thread
+    // Q and K rows are fetched and staged by the first head's waves alone when a
+    // workgroup holds two heads of four waves: those waves win the issue arbitration
+    // on their SIMDs and finish the solve first, while the other head's waves, which
+    // finish it last, go straight on to it after the barrier.
+    constexpr bool SPLIT = NW == 8;
+    constexpr int NTS = SPLIT ? NT / 2 : NT; // threads that fetch and stage Q and K
+    constexpr int NQ = kC * VPR / NTS;       // prefetched Q (and K) vectors per such thread
     constexpr int NNL = HG * (NWH - 1);      // waves that are not the first of their head
-    static_assert(NQ * NT == kC * VPR, "Q/K prefetch must divide evenly");
+    static_assert(NQ * NTS == kC * VPR, "Q/K prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
 
     const int G = a.H_v / a.H_k;
@@ -342,14 +348,16 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         const int tok = lo + b0, L = e0 - b0;
         const __bf16* qb = qg + ((size_t)tok * a.H_k + kh) * DK;
         const __bf16* kb = kg + ((size_t)tok * a.H_k + kh) * DK;
+        if (!SPLIT || wv < NW / 2) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned r = i / VPR, vi = i % VPR;
-            const uint32_t off = (r * (unsigned)a.H_k * DK + vi * 8) * 2u;
-            const bool in = (int)r < L;
-            pq[j] = in ? ld16(qb, off) : make_uint4(0u, 0u, 0u, 0u);
-            pk[j] = in ? ld16(kb, off) : make_uint4(0u, 0u, 0u, 0u);
+            for (int j = 0; j < NQ; ++j) {
+                const unsigned i = t + NTS * j;
+                const unsigned r = i / VPR, vi = i % VPR;
+                const uint32_t off = (r * (unsigned)a.H_k * DK + vi * 8) * 2u;
+                const bool in = (int)r < L;
+                pq[j] = in ? ld16(qb, off) : make_uint4(0u, 0u, 0u, 0u);
+                pk[j] = in ? ld16(kb, off) : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         if (lead) {
             const unsigned s = t & 63;
@@ -383,12 +391,14 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     // chunk c - 1.  Doing it before phase 3 issues its stores keeps the wait for the
     // loads from waiting for those.
     auto stage_q = [&](int c, unsigned t) {
+        if (!SPLIT || wv < NW / 2) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned r = i / VPR, vi = i % VPR;
-            const unsigned col = (vi * 8) ^ (r & 8);
-            *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = bf16x8_to_f16x8(pq[j]);
+            for (int j = 0; j < NQ; ++j) {
+                const unsigned i = t + NTS * j;
+                const unsigned r = i / VPR, vi = i % VPR;
+                const unsigned col = (vi * 8) ^ (r & 8);
+                *reinterpret_cast<uint4*>(sm.q + r * SM::QLD + col) = bf16x8_to_f16x8(pq[j]);
+            }
         }
         if (lead) {                          // gates of this head, lane = token
             constexpr float kLog2e = 1.4426950408889634f;
@@ -413,12 +423,14 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     // the barrier that follows chunk c - 1's state update.
     auto stage_k = [&](int c, unsigned t) {
         _Float16* kb = sm.k[KB == 2 ? (c & 1) : 0];
+        if (!SPLIT || wv < NW / 2) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const unsigned i = t + NT * j;
-            const unsigned r = i / VPR, vi = i % VPR;
-            const unsigned col = (vi * 8) ^ (r & 8);
-            *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = bf16x8_to_f16x8(pk[j]);
+            for (int j = 0; j < NQ; ++j) {
+                const unsigned i = t + NTS * j;
+                const unsigned r = i / VPR, vi = i % VPR;
+                const unsigned col = (vi * 8) ^ (r & 8);
+                *reinterpret_cast<uint4*>(kb + r * SM::QLD + col) = bf16x8_to_f16x8(pk[j]);
+            }
         }
     };
     // Q and K loads run a chunk ahead of their staging: right after phase 1 of chunk

@@ -230,12 +230,6 @@ struct Smem {
     } hd[HG];
 };
 
-// Tile tt of phase 1: 0..9 the lower blocks of K K^T, 10..19 those of Q K^T.
-__device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
-    i = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-    j = t - i * (i + 1) / 2;
-}
-
 // Waves per SIMD the register allocation must allow: with one K buffer two workgroups
 // share a compute unit.
 template <int DV, int HG, int KB>
@@ -519,61 +513,77 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 th[(r + 1) * SM::BLD + jc] = (unsigned short)(w >> 16);
             }
         } else {
-            constexpr int NTI = (16 + NNL - 1) / NNL;
             // index among the others.  Waves wv and wv ^ 4 share a SIMD (probed); with two
             // heads of four waves the first waves are 0 and 5, and their SIMD partners 4
             // and 1 take the two slots with two tiles, the other four waves three each.
             const int nl = NW == 8 ? (int)((0x32051040u >> (4 * wv)) & 15u)
                                    : hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);
+            // Wave nl of the NNL others: the off-diagonal blocks (i, j) number nl, nl +
+            // NNL, ... of both K K^T (-> -A_ij) and Q K^T (-> P_ij), which share the K_j
+            // reads and the decay factors, then the diagonal blocks (b, b), b = nl, nl +
+            // NNL, ... < 4, of Q K^T.  Every wave runs the same sequence of tile kinds,
+            // so the compiler can overlap them.
+            static_assert(6 % NNL == 0, "the off-diagonal blocks must divide evenly");
+            const int sw = (8 * g4) ^ (li & 8);
 #pragma unroll
-            for (int n = 0; n < NTI; ++n) {
-                const int tt = nl + NNL * n;     // wave-uniform: 0..5 K K^T, 6..15 Q K^T
-                if (tt >= 16) break;
-                int i, j;
-                if (tt < 6) {                    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                    i = 1 + (tt >= 1) + (tt >= 3);
-                    j = tt - (i - 1) * i / 2;
-                } else {
-                    tile_ij(tt - 6, i, j);
-                }
-                const _Float16* X = tt < 6 ? kb : sm.q;
-                f16x8 fa[KS_DK], fb[KS_DK];
+            for (int m = 0; m < 6 / NNL; ++m) {
+                const int o = nl + NNL * m;      // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                const int i = 1 + (o >= 1) + (o >= 3), j = o - (i - 1) * i / 2;
+                f16x8 fkj[KS_DK], fki[KS_DK], fqi[KS_DK];
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
-                    fa[kk] = ld8h(kb + (16 * j + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
-                    fb[kk] = ld8h(X + (16 * i + li) * SM::QLD + ((8 * g4) ^ (li & 8)) + 32 * kk);
+                    fkj[kk] = ld8h(kb + (16 * j + li) * SM::QLD + sw + 32 * kk);
+                    fki[kk] = ld8h(kb + (16 * i + li) * SM::QLD + sw + 32 * kk);
+                    fqi[kk] = ld8h(sm.q + (16 * i + li) * SM::QLD + sw + 32 * kk);
                 }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 aK = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32h(fa[kk], fb[kk], acc);
-                // lane (li, g4): acc[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    aK = mma32h(fkj[kk], fki[kk], aK);
+                    aQ = mma32h(fkj[kk], fqi[kk], aQ);
+                }
+                // lane (li, g4): aX[e] = (X K^T)[r][s], r = 16 i + li, s = 16 j + 4 g4 + e
                 const int r = 16 * i + li, s0 = 16 * j + 4 * g4;
 #pragma unroll
                 for (int x = 0; x < HG; ++x) {
                     typename SM::Head& hx = sm.hd[x];
                     const float* gx = hx.gate[buf];
-                    if (i != j) {
-                        // block (i, j) below the diagonal: e^(G_r - G_s) = FS_r c TE_s with
-                        // c = e^(G_16i - G_16j+15)
-                        const float c2 = gx[GATE_G2 * kC + 16 * i] - gx[GATE_G2 * kC + 16 * j + 15];
-                        const float fr = gx[GATE_FS * kC + r] * __builtin_amdgcn_exp2f(c2);
-                        const f32x4 te = *reinterpret_cast<const f32x4*>(gx + GATE_TE * kC + s0);
-                        if (tt < 6) {            // -A_ij = -beta_r (K K^T)_rs D_rs
-                            const Split4h sp = split4h(acc * te * -(fr * gx[GATE_BET * kC + r]));
-                            st4h(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
-                            st4h(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
-                        } else {
-                            st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(acc * te * (a.scale * fr)));
-                        }
-                    } else {                     // a diagonal block of Q K^T: s <= r only
-                        const float G2r = gx[GATE_G2 * kC + r];
-                        const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
-                        f32x4 pd;
+                    // below the diagonal: e^(G_r - G_s) = FS_r c TE_s, c = e^(G_16i - G_16j+15)
+                    const float c2 = gx[GATE_G2 * kC + 16 * i] - gx[GATE_G2 * kC + 16 * j + 15];
+                    const float fr = gx[GATE_FS * kC + r] * __builtin_amdgcn_exp2f(c2);
+                    const f32x4 te = *reinterpret_cast<const f32x4*>(gx + GATE_TE * kC + s0);
+                    // -A_ij = -beta_r (K K^T)_rs D_rs
+                    const Split4h sp = split4h(aK * te * -(fr * gx[GATE_BET * kC + r]));
+                    st4h(hx.sol[blk(i, j)][0] + li * SM::BLD + 4 * g4, sp.hi);
+                    st4h(hx.sol[blk(i, j)][1] + li * SM::BLD + 4 * g4, sp.lo);
+                    st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(aQ * te * (a.scale * fr)));
+                }
+            }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            pd[e] = s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f;
-                        st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(pd));
-                    }
+            for (int m = 0; m < (4 + NNL - 1) / NNL; ++m) {
+                const int b = nl + NNL * m;      // a diagonal block of Q K^T: s <= r only
+                if (b >= 4) break;
+                f16x8 fkb[KS_DK], fqb[KS_DK];
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    fkb[kk] = ld8h(kb + (16 * b + li) * SM::QLD + sw + 32 * kk);
+                    fqb[kk] = ld8h(sm.q + (16 * b + li) * SM::QLD + sw + 32 * kk);
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) acc = mma32h(fkb[kk], fqb[kk], acc);
+                const int r = 16 * b + li, s0 = 16 * b + 4 * g4;
+#pragma unroll
+                for (int x = 0; x < HG; ++x) {
+                    typename SM::Head& hx = sm.hd[x];
+                    const float* gx = hx.gate[buf];
+                    const float G2r = gx[GATE_G2 * kC + r];
+                    const f32x4 G2s = *reinterpret_cast<const f32x4*>(gx + GATE_G2 * kC + s0);
+                    f32x4 pd;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pd[e] = s0 + e <= r ? a.scale * acc[e] * __builtin_amdgcn_exp2f(G2r - G2s[e]) : 0.f;
+                    st4h(hx.p[blk(b, b)] + li * SM::BLD + 4 * g4, cvt4h(pd));
                 }
             }
         }

@@ -78,9 +78,10 @@ gdn_status check_decode(const gdn_shape* shape, int32_t num_rows, const void* q,
     if (num_rows < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_rows %d is negative", num_rows);
     if (num_slots < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots %d is negative", num_slots);
     if (num_rows == 0) return GDN_OK;
-    if ((int64_t)num_rows * shape->num_v_heads > 0x7fffffffLL)
-        return fail(GDN_ERR_UNSUPPORTED, "num_rows %d x num_v_heads %d exceeds the launch grid", num_rows,
-                    shape->num_v_heads);
+    // one workgroup per 64 value columns of each (row, value head)
+    if ((int64_t)num_rows * shape->num_v_heads * (shape->d_v / 64) > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "num_rows %d x num_v_heads %d x d_v / 64 exceeds the launch grid",
+                    num_rows, shape->num_v_heads);
     return check_ptrs({{"q", q, 16}, {"k", k, 16}, {"v", v, 16}, {"g", g, 4}, {"beta", beta, 4},
                        {"o", o, 16}, {"state_pool", state_pool, 16}, {"slot_in", slot_in, 4},
                        {"slot_out", slot_out, 4}});

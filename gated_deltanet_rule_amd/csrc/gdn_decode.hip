@@ -1,7 +1,7 @@
 // gdn_decode.hip -- packed recurrent decode for gfx950 (MI355X).
 //
-// One workgroup of 1024 threads advances the state of one (row, value head) by one
-// token ("[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
+// A workgroup of 256 threads advances 64 value columns of the state of one (row, value
+// head) by one token ("[Model] Enable batch-invariant mixed decode and prefill for Qwen GDN",
 // sections "Why" and "How": cached rows take the packed recurrent decode path), or by
 // tokens_per_row tokens in order for a multi-token verify row: the state stays in
 // registers between the row's tokens and is written after each token to that token's
@@ -11,16 +11,17 @@
 //
 //     S <- exp(g) S;   u = beta (v - S^T k);   S <- S + k u^T;   o = scale S^T q
 //
-// Thread layout: a state row (d_v floats) is covered by d_v/4 threads holding one
-// float4 each; the 1024 threads form 1024/(d_v/4) row groups, and row group r holds
-// rows r, r + RG, r + 2 RG, ...  Large workgroups keep few state rows per thread, so
-// two workgroups fit on a compute unit and the later ones' loads overlap the earlier
-// ones' stores (a cold in-place update of 64 KiB states runs at the speed of a plain
-// read-modify-write of the same blocks).  The two reductions over d_k (S^T k and
-// S^T q) are per-thread partial sums followed by a fixed-order sum over the row groups
-// through LDS, so the result does not depend on anything but the row's own data: a
-// row's output and state are bitwise the same in any batch, at any position, and a
-// verify row equals the same tokens decoded one call at a time.
+// The value columns of S, u and o are independent (both reductions run over d_k), so a
+// state is split by columns over d_v / 64 workgroups.  Thread layout: a state row's 64
+// columns are covered by 16 threads holding one float4 each; the 256 threads form 16
+// row groups, and row group r holds rows r, r + 16, r + 32, ...  Small workgroups (32
+// KiB of state each, eight to a compute unit) start and finish one by one, so loads
+// and stores of different workgroups stay interleaved; one workgroup of 1024 threads
+// per 64 KiB state ran 2-3 % slower.  The two reductions over d_k (S^T k and S^T q)
+// are per-thread partial sums followed by a fixed-order sum over the row groups through
+// LDS, so the result does not depend on anything but the row's own data: a row's
+// output and state are bitwise the same in any batch, at any position, and a verify
+// row equals the same tokens decoded one call at a time.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -68,7 +69,8 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float4 v) {
     *reinterpret_cast<bf16x4*>(p) = x;
 }
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kCols = 64;            // value columns per workgroup
 
 // State traffic is touched once per call: stream it with non-temporal loads and
 // stores so it neither evicts nor waits on cache lines other work could reuse.
@@ -84,12 +86,15 @@ __device__ __forceinline__ void store_state(float* p, float4 v) {
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-    constexpr int TPR = DV / 4;          // threads per state row
+    constexpr int TPR = kCols / 4;       // threads per state row slice
     constexpr int RG = kThreads / TPR;   // row groups
     constexpr int R = DK / RG;           // rows per thread
-    static_assert(R * RG == DK && TPR * RG == kThreads, "bad decode tiling");
+    constexpr int NCW = DV / kCols;      // workgroups per (row, head)
+    static_assert(R * RG == DK && TPR * RG == kThreads && NCW * kCols == DV && 2 * DK <= kThreads,
+                  "bad decode tiling");
 
-    const int unit = blockIdx.x;
+    const int unit = blockIdx.x / NCW;
+    const int col0 = kCols * (blockIdx.x - unit * NCW);
     const int b = unit / a.H_v;
     const int h = unit - b * a.H_v;
     const int kh = h / (a.H_v / a.H_k);
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (sin < 0 || sin >= a.num_slots) {          // padding row
         for (int t = 0; t < NTOK; ++t) {
             T* o = static_cast<T*>(a.o) + ((size_t)(b * NTOK + t) * a.H_v + h) * DV;
-            if (tid < DV) o[tid] = from_f32<T>(0.f);
+            if (tid < kCols) o[col0 + tid] = from_f32<T>(0.f);
         }
         return;
     }
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     float4 s[R];
 #pragma unroll
     for (int m = 0; m < R; ++m)
-        s[m] = load_state(src + (size_t)(rg + RG * m) * DV + 4 * c4);
+        s[m] = load_state(src + (size_t)(rg + RG * m) * DV + col0 + 4 * c4);
 
     __shared__ float kq[2][DK];
     __shared__ float4 red[2][RG][TPR];
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const T* qp = static_cast<const T*>(a.q) + (row * a.H_k + kh) * DK;
         if (tid < DK) kq[0][tid] = to_f32(kp[tid]);
         else if (tid < 2 * DK) kq[1][tid - DK] = to_f32(qp[tid - DK]);
-        const float4 vv = load4<T>(static_cast<const T*>(a.v) + row * a.H_v * DV + (size_t)h * DV + 4 * c4);
+        const float4 vv = load4<T>(static_cast<const T*>(a.v) + row * a.H_v * DV + (size_t)h * DV + col0 + 4 * c4);
         const float alpha = expf(a.g[row * a.H_v + h]);
         const float beta = a.beta[row * a.H_v + h];
         __syncthreads();
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             float* dst = a.pool + ((size_t)sout * a.H_v + h) * (size_t)(DK * DV);
 #pragma unroll
             for (int m = 0; m < R; ++m)
-                store_state(dst + (size_t)(rg + RG * m) * DV + 4 * c4, s[m]);
+                store_state(dst + (size_t)(rg + RG * m) * DV + col0 + 4 * c4, s[m]);
         }
         red[1][rg][c4] = po;
         __syncthreads();
@@ -178,14 +183,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
                 to.x += x.x; to.y += x.y; to.z += x.z; to.w += x.w;
             }
             const float sc = a.scale;
-            store4<T>(o + 4 * c4, make_float4(sc * to.x, sc * to.y, sc * to.z, sc * to.w));
+            store4<T>(o + col0 + 4 * c4, make_float4(sc * to.x, sc * to.y, sc * to.z, sc * to.w));
         }
     }
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-    const unsigned blocks = (unsigned)a.num_rows * (unsigned)a.H_v;
+    const unsigned blocks = (unsigned)a.num_rows * (unsigned)a.H_v * (unsigned)(DV / kCols);
     hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -18,8 +18,9 @@
 //     S  <- gamma_last S + K^T (diag(e^(G_last - G)) U)
 //
 // One workgroup owns one sequence and HG value heads that share a key head, and walks
-// the sequence's chunks in order.  Per value head, d_v is split into 32-column strips,
-// one wave each; a wave keeps its strip of S (d_k x 32, fp32) in MFMA accumulators
+// the sequence's chunks in order.  Per value head, d_v is split into 32-column strips
+// (16-column ones when the call has no more chains than compute units), one wave
+// each; a wave keeps its strip of S (d_k x 32 or d_k x 16, fp32) in MFMA accumulators
 // for the whole sequence.  The d_v columns of S, R, U and O are independent, so
 // strips never exchange data.  The solve runs on 16-row blocks of the chunk:
 //     U_i = T_ii (R_i - sum_{j<i} A_ij U_j),   T_ii = (I + A_ii)^-1 (16 x 16)
@@ -232,15 +233,19 @@ struct Smem {
 
 // Waves per SIMD the register allocation must allow: with one K buffer two workgroups
 // share a compute unit.
-template <int DV, int HG, int KB>
+template <int DV, int HG, int KB, int SW>
 constexpr int waves_per_simd() {
-    return (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 > 1 ? (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 : 1;
+    return SW == 16 ? 2 : (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 > 1 ? (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 : 1;
 }
 
-template <int DK, int DV, int HG, int KB>
-__global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void chunk_kernel(PrefillArgs a) {
+// SW is the width of a wave's strip of value columns: 32, or 16 for calls whose
+// workgroups each get a compute unit of their own (twice the waves per head, half the
+// work per wave along the chain of chunks).
+template <int DK, int DV, int HG, int KB, int SW>
+__global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>())) void chunk_kernel(PrefillArgs a) {
     using SM = Smem<DK, DV, HG, KB>;
-    constexpr int NWH = DV / 32;             // waves per value head
+    constexpr int NWH = DV / SW;             // waves per value head
+    constexpr int NTL = SW / 16;             // 16-column tiles per strip
     constexpr int NW = HG * NWH;             // waves
     constexpr int NT = NW * 64;              // threads
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     // workgroup holds two heads of four waves: those waves win the issue arbitration
     // on their SIMDs and finish the solve first, while the other head's waves, which
     // finish it last, go straight on to it after the barrier.
-    constexpr bool SPLIT = NW == 8;
+    constexpr bool SPLIT = HG == 2 && NW == 8;
     constexpr int NTS = SPLIT ? NT / 2 : NT; // threads that fetch and stage Q and K
     constexpr int NQ = kC * VPR / NTS;       // prefetched Q (and K) vectors per such thread
     constexpr int NNL = HG * (NWH - 1);      // waves that are not the first of their head
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     int lane = tid & 63;
     const int hh = wv / NWH;                 // this wave's head within the group
     const int h = h0 + hh;
-    const int col0 = 32 * (wv - hh * NWH);
+    const int col0 = SW * (wv - hh * NWH);
     // The "first" wave of each head (the one that scans the gates and inverts the
     // diagonal blocks) is wave hh of the head, so that the heads' first waves sit on
     // different SIMDs (waves go to SIMDs by index modulo 4).
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 
     const size_t SE = (size_t)DK * DV;
     // state strip: Sacc[mt][nt] holds S[16 mt + 4 g + i][col0 + 16 nt + li]
-    f32x4 Sacc[MT_S][2];
+    f32x4 Sacc[MT_S][NTL];
     const int isl = a.init_slot ? a.init_slot[seq] : -1;
     if (isl >= 0 && isl < a.num_slots) {
         const int li = lane & 15, g4 = lane >> 4;
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     Sacc[mt][nt][i] = src[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li];
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     int lo, len;
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
     uint4 pq[NQ], pk[NQ];
     // this wave's V strip of a chunk in the A-operand layout of the 16x16x16 identity
     // product: pv[mt][nt] = V[16 mt + li][col0 + 16 nt + 4 g4 .. + 3]
-    bf16x4 pv[4][2];
+    bf16x4 pv[4][NTL];
     float gpf = 0.f, bpf = 0.f;
     auto ld16 = [](const void* base, uint32_t off) {
         return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTL; ++nt) {
                 const unsigned r = 16u * mt + li;
                 const uint32_t off = (r * (unsigned)a.H_v * DV + 16u * nt + 4u * g4) * 2u;
                 pv[mt][nt] = (int)r < L ? *reinterpret_cast<const bf16x4*>(vb + off) : bf16x4{};
@@ -515,19 +520,20 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         } else {
             // index among the others.  Waves wv and wv ^ 4 share a SIMD (probed); with two
             // heads of four waves the first waves are 0 and 5, and their SIMD partners 4
-            // and 1 take the two slots with two tiles, the other four waves three each.
-            const int nl = NW == 8 ? (int)((0x32051040u >> (4 * wv)) & 15u)
-                                   : hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);
-            // Wave nl of the NNL others: the off-diagonal blocks (i, j) number nl, nl +
-            // NNL, ... of both K K^T (-> -A_ij) and Q K^T (-> P_ij), which share the K_j
-            // reads and the decay factors, then the diagonal blocks (b, b), b = nl, nl +
-            // NNL, ... < 4, of Q K^T.  Every wave runs the same sequence of tile kinds,
-            // so the compiler can overlap them.
-            static_assert(6 % NNL == 0, "the off-diagonal blocks must divide evenly");
+            // and 1 take the two slots with an off-diagonal pair alone, the other four
+            // waves a pair and a diagonal block each.
+            const int nl = SPLIT ? (int)((0x32051040u >> (4 * wv)) & 15u)
+                                 : hh * (NWH - 1) + (wi < hh % NWH ? wi : wi - 1);
+            // The ten jobs, six off-diagonal block pairs (i, j) (K K^T -> -A_ij and Q K^T
+            // -> P_ij, which share the K_j reads and the decay factors) and then the four
+            // diagonal blocks (b, b) of Q K^T, go round robin to the NNL others: wave nl
+            // takes jobs nl, nl + NNL, ...  Every wave runs the same sequence of tile
+            // kinds, so the compiler can overlap them.
             const int sw = (8 * g4) ^ (li & 8);
 #pragma unroll
-            for (int m = 0; m < 6 / NNL; ++m) {
+            for (int m = 0; m < (6 + NNL - 1) / NNL; ++m) {
                 const int o = nl + NNL * m;      // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                if (o >= 6) break;
                 const int i = 1 + (o >= 1) + (o >= 3), j = o - (i - 1) * i / 2;
                 f16x8 fkj[KS_DK], fki[KS_DK], fqi[KS_DK];
 #pragma unroll
@@ -559,9 +565,10 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                     st4h(hx.p[blk(i, j)] + li * SM::BLD + 4 * g4, cvt4h(aQ * te * (a.scale * fr)));
                 }
             }
+            const int b0 = (nl + 6 * NNL - 6) % NNL;   // this wave's first job past the pairs, less 6
 #pragma unroll
             for (int m = 0; m < (4 + NNL - 1) / NNL; ++m) {
-                const int b = nl + NNL * m;      // a diagonal block of Q K^T: s <= r only
+                const int b = b0 + NNL * m;      // a diagonal block of Q K^T: s <= r only
                 if (b >= 4) break;
                 f16x8 fkb[KS_DK], fqb[KS_DK];
 #pragma unroll
@@ -592,22 +599,23 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         // O is accumulated transposed (value columns as rows), so that a lane ends up
         // with four consecutive columns of one output row.
         const float* gt = hd.gate[buf];
-        f32x4 Racc[4][2], Oacc[4][2];
+        f32x4 Racc[4][NTL], Oacc[4][NTL];
         {
-            f16x8 Sb[KS_DK][2];
+            f16x8 Sb[KS_DK][NTL];
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) Sb[kk][nt] = state_frag(Sacc[2 * kk][nt], Sacc[2 * kk + 1][nt]);
+                for (int nt = 0; nt < NTL; ++nt) Sb[kk][nt] = state_frag(Sacc[2 * kk][nt], Sacc[2 * kk + 1][nt]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                Racc[mt][0] = Racc[mt][1] = Oacc[mt][0] = Oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) Racc[mt][nt] = Oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS_DK; ++kk) {
                     const f16x8 ak = row_fromc(kb + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
                     const f16x8 aq = row_fromc(sm.q + (16 * mt + li) * SM::QLD, kk, g4, li & 8);
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
+                    for (int nt = 0; nt < NTL; ++nt) {
                         Racc[mt][nt] = mma32h(ak, Sb[kk][nt], Racc[mt][nt]);
                         Oacc[mt][nt] = mma32h(Sb[kk][nt], aq, Oacc[mt][nt]);
                     }
@@ -618,14 +626,14 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] *= gam_last;
+            for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] *= gam_last;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const f32x4 gam = *reinterpret_cast<const f32x4*>(gt + GATE_GAM * kC + 16 * mt + 4 * g4);
             const f32x4 bet = *reinterpret_cast<const f32x4*>(gt + GATE_BET * kC + 16 * mt + 4 * g4);
             const float sg = a.scale * gt[GATE_GAM * kC + 16 * mt + li];   // output row 16 mt + li
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTL; ++nt) {
                 Oacc[mt][nt] *= sg;
                 // + V through V I, onto -gamma Z
                 Racc[mt][nt] = mma16(pv[mt][nt], ident, -gam * Racc[mt][nt]);
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         //      U_0..U_i exist; then the state update
         __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
         const int bo = li * SM::BLD + 4 * g4;   // the lane's offset in a 16x16 block
-        f16x4 Uh[4][2], Ul[4][2];             // U blocks as fp16 hi + lo pairs; hi alone in
+        f16x4 Uh[4][NTL], Ul[4][NTL];             // U blocks as fp16 hi + lo pairs; hi alone in
                                               // the output product
         // X_i = R_i - sum_{j<i} A_ij U_j accumulates in Racc[i] as soon as each U_j exists
         // (right-looking), so that only one block product lies between U_i and
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         auto upd1 = [&](int i, int j) __attribute__((always_inline)) {
             const f16x8 a2 = cat8h(ld4h_single(hd.sol[blk(i, j)][0] + bo), ld4h_single(hd.sol[blk(i, j)][1] + bo));
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTL; ++nt) {
                 Racc[i][nt] = mma32h(a2, cat8h(Uh[j][nt], Uh[j][nt]), Racc[i][nt]);
                 Racc[i][nt] = mma32h(a2, cat8h(Ul[j][nt], Ul[j][nt]), Racc[i][nt]);
             }
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTL; ++nt) {
                 // U_i = T_ii X_i, both single fp16 values
                 const f16x4 th = ld4h_single(hd.sol[blk(i, i)][0] + bo);
                 const f32x4 U = mma16h(th, cvt4h(Racc[i][nt]), f32x4{0.f, 0.f, 0.f, 0.f});
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 const f16x8 ah = cat8h(ld4h_single(hd.sol[blk(3, 0)][0] + bo), ld4h_single(hd.sol[blk(3, 1)][0] + bo));
                 const f16x8 al = cat8h(ld4h_single(hd.sol[blk(3, 0)][1] + bo), ld4h_single(hd.sol[blk(3, 1)][1] + bo));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NTL; ++nt) {
                     const f16x8 uh = cat8h(Uh[0][nt], Uh[1][nt]);
                     const f16x8 ul = cat8h(Ul[0][nt], Ul[1][nt]);
                     Racc[3][nt] = mma32h(ah, uh, Racc[3][nt]);
@@ -700,7 +708,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 const f16x4 p0 = ld4h_single(hd.p[blk(i, j0)] + bo);
                 const f16x8 pp = cat8h(p0, j1 <= i ? ld4h_single(hd.p[blk(i, j1)] + bo) : zero4);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NTL; ++nt)
                     Oacc[i][nt] = mma32h(cat8h(Uh[j0][nt], Uh[j1 <= i ? j1 : j0][nt]), pp, Oacc[i][nt]);
             }
             // Lane (li, g4) holds O[16 i + li][col0 + 16 nt + 4 g4 + e].  One row swap
@@ -708,7 +716,13 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
             // first register trade places with rows 0 and 2 of the second) leaves an
             // even group with the nt = 0 columns 4 g4 .. 4 g4 + 7 and an odd group with
             // the nt = 1 columns 12 + 4 g4 .. 12 + 4 g4 + 7: one 16-byte store per lane.
-            {
+            // A 16-column strip stores its four columns per lane as they are.
+            if constexpr (NTL == 1) {
+                const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][0], bf16x4));
+                const int r = 16 * i + li;
+                const uint32_t off = (uint32_t)(r * a.H_v * DV + 4 * g4) * 2u;
+                if (r < L) *reinterpret_cast<uint2*>(reinterpret_cast<char*>(obase) + off) = x;
+            } else {
                 const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][0], bf16x4));
                 const uint2 y = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][1], bf16x4));
                 const auto s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
@@ -725,13 +739,13 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
         // first; then the K^T reads (transposing reads of the K rows) run two steps
         // ahead of the MFMAs that use them.
         const _Float16* ktr = kb + (lane >> 2) * SM::QLD + ((4 * (lane & 3)) ^ ((lane >> 2) & 8));
-        f16x8 bh[2][2], bl[2][2];            // the decayed U as fp16 hi + lo pairs
+        f16x8 bh[2][NTL], bl[2][NTL];            // the decayed U as fp16 hi + lo pairs
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const f32x4 kd0 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 4 * g4);
             const f32x4 kd1 = *reinterpret_cast<const f32x4*>(gt + GATE_KDEC * kC + 32 * kk + 16 + 4 * g4);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NTL; ++nt) {
                 const Split4h s0 = split4h(Racc[2 * kk][nt] * kd0);
                 const Split4h s1 = split4h(Racc[2 * kk + 1][nt] * kd1);
                 bh[kk][nt] = cat8h(s0.hi, s1.hi);
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
                 if (t + 2 < NSTEP) ka[(t + 2) % 3] = kfrag(t + 2);
                 const int mt = t >> 1, kk = t & 1;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NTL; ++nt) {
                     Sacc[mt][nt] = mma32h(ka[t % 3], bh[kk][nt], Sacc[mt][nt]);
                     Sacc[mt][nt] = mma32h(ka[t % 3], bl[kk][nt], Sacc[mt][nt]);
                 }
@@ -764,7 +778,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
             for (int t = 0; t < NSTEP; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // four MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTL, 0);   // the step's MFMAs
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -798,7 +812,7 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
                     for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
+                        for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
@@ -814,28 +828,28 @@ __global__ __launch_bounds__(HG * DV * 2, (waves_per_simd<DV, HG, KB>())) void c
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
     }
 }
 
-template <int DK, int DV, int HG>
+template <int DK, int DV, int HG, int SW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const int G = a.H_v / a.H_k;
     const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG);
     constexpr int KB = HG == 1 ? 1 : 2;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG, KB>), dim3(blocks), dim3(HG * DV * 2), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG, KB, SW>), dim3(blocks), dim3(HG * DV / SW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int HG>
+template <int HG, int SW>
 hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, HG>(a, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, HG>(a, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, HG>(a, stream);
-    return launch_typed<64, 64, HG>(a, stream);
+    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, HG, SW>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, HG, SW>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, HG, SW>(a, stream);
+    return launch_typed<64, 64, HG, SW>(a, stream);
 }
 
 // Compute units of the current device (the launch goes to it), read once per device.
@@ -859,12 +873,17 @@ int device_cus() {
 // with few sequences (a varlen batch of a few long prompts, the prefill part of a
 // mixed step) is bound by the length of its longest chain, and one head per
 // workgroup runs that chain with four waves on the compute unit instead of eight.
-// Both shapes run the same arithmetic per element, so a sequence's results are
-// bitwise the same whichever shape its call takes.
+// When even the (sequence, value head) chains do not outnumber the compute units,
+// each workgroup has a compute unit to itself and its head gets eight waves of
+// 16-column strips, which halves each wave's share of the chain's products.  All
+// shapes run the same arithmetic per element, so a sequence's results are bitwise
+// the same whichever shape its call takes.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int G = a.H_v / a.H_k;
-    if (G % 2 == 0 && (int64_t)a.num_seqs * a.H_k * (G / 2) >= device_cus()) return launch_dims<2>(a, stream);
-    return launch_dims<1>(a, stream);
+    const int64_t units = (int64_t)a.num_seqs * a.H_v;   // (sequence, value head) chains
+    if (G % 2 == 0 && units / 2 >= device_cus()) return launch_dims<2, 32>(a, stream);
+    if (units <= device_cus()) return launch_dims<1, 16>(a, stream);
+    return launch_dims<1, 32>(a, stream);
 }
 
 }  // namespace gdn

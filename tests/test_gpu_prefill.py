@@ -155,9 +155,11 @@ def test_prefill_batch_invariance():
 def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
     """With two value heads per key head the bf16 kernel gives each workgroup both
     heads when the call has enough (sequence, key head) pairs to fill the compute
-    units, and one head otherwise.  The same sequences alone (few pairs: one head per
-    workgroup) and inside a batch that fills the GPU (two heads per workgroup) give
-    bitwise equal outputs, final states and exports."""
+    units, one head with 32-column strips when its (sequence, value head) chains
+    outnumber the compute units, and one head with 16-column strips otherwise.  The
+    same sequences alone (16-column strips), in a middling batch (32-column strips, one
+    head) and inside a batch that fills the GPU (two heads per workgroup) give bitwise
+    equal outputs, final states and exports."""
     H_k, H_v = 16, 32
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = -(-cus // H_k)                               # sequences for a full launch of head pairs
@@ -186,6 +188,24 @@ def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
         assert torch.equal(dsolo["pool"][2 * n + 3], dbase["pool"][int(base.final_slot[i])]), i
         n_i = offs[i + 1] - offs[i]
         assert torch.equal(exp_solo[:n_i], exp_all[offs[i]:offs[i + 1]]), i
+    # the first m sequences: more chains than compute units, fewer head pairs
+    m = cus // H_v + 1
+    assert m * H_v > cus and m * H_k < cus and m < n
+    mid = W.make_workload("shape2", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=lengths[:m],
+                          num_slots=2 * n + 4, export_grid=64)
+    b = int(cu[m])
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(mid, name, getattr(base, name)[:b].copy())
+    mid.pool = base.pool
+    mid.init_slot = base.init_slot[:m].copy()
+    mid.final_slot = base.final_slot[:m].copy()
+    dmid = to_device(mid)
+    exp_mid, _ = run_prefill(mid, dmid)
+    torch.cuda.synchronize()
+    assert torch.equal(dmid["o"], dbase["o"][:b])
+    fin = torch.as_tensor(mid.final_slot, device=dmid["pool"].device).long()
+    assert torch.equal(dmid["pool"][fin], dbase["pool"][fin])
+    assert torch.equal(exp_mid[:offs[m]], exp_all[:offs[m]])
     # and the full batch against the oracle
     check_prefill(base, prefill_reference(base), dbase["o"], dbase["pool"], exp_all)
 

@@ -61,5 +61,8 @@ size_t prefill_workspace_bytes(int H_v, int dtype, int num_seqs, int64_t total_t
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // The bf16 kernel (gdn_prefill_bf16.hip); launch_prefill routes bf16 calls to it.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// Compute units of the current device, read once per device (gdn_prefill_bf16.hip):
+// the prefill launchers pick their workgroup shape by it.
+int device_cus();
 
 }  // namespace gdn

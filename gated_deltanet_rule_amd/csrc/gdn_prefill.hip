@@ -101,10 +101,14 @@ struct ScanSmem {
 
 // ---------------------------------------------------------------- the scan kernel
 
-template <int DK, int DV>
-__global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
+// SW is the width of a wave's strip of value columns: 32, or 16 for calls whose
+// workgroups each get a compute unit of their own (twice the waves, half the products
+// per wave along the chain of chunks).
+template <int DK, int DV, int SW>
+__global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     using SM = ScanSmem<DK, DV>;
-    constexpr int NW = DV / 32;              // waves (one 32-column strip each)
+    constexpr int NW = DV / SW;              // waves (one strip each)
+    constexpr int NTL = SW / 16;             // 16-column tiles per strip
     constexpr int NT = NW * 64;              // threads
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
     constexpr int KS_DK = DK / 4;            // k steps over d_k
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
     constexpr int VPRV = DV / 4;             // 16-byte vectors per V row
     constexpr int NPV = kC * VPRV / NT;      // prefetched V vectors per thread
     constexpr int TPW = (16 + NW - 1) / NW;  // 16x16 tiles of a 64x64 matrix per wave
-    constexpr int NVF = KS_C * 2;            // V fragments per wave
+    constexpr int NVF = KS_C * NTL;          // V fragments per wave
     static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
@@ -126,11 +130,11 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     int lane = tid & 63;
-    const int col0 = 32 * wv;
+    const int col0 = SW * wv;
 
     const size_t SE = (size_t)DK * DV;
     // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
-    f32x4 Sacc[MT_S][2];
+    f32x4 Sacc[MT_S][NTL];
     const int isl = a.init_slot ? a.init_slot[seq] : -1;
     if (isl >= 0 && isl < a.num_slots) {
         const int li = lane & 15, g4 = lane >> 4;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     Sacc[mt][nt][i] = src[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li];
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     int lo, len;
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KS_C; ++kk)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) vcur[kk * 2 + nt] = sm.v[k_nat(kk, g4) * SM::VLD + col0 + 16 * nt + li];
+            for (int nt = 0; nt < NTL; ++nt) vcur[kk * NTL + nt] = sm.v[k_nat(kk, g4) * SM::VLD + col0 + 16 * nt + li];
         if (wv == 0) {
             const float gs = sm.graw[lane];
             const float bs = sm.braw[lane];
@@ -362,28 +366,29 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 Uacc[4][2];
+        f32x4 Uacc[4][NTL];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            Uacc[mt][0] = Uacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) Uacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
                 if (4 * kk > 16 * mt + 15) continue;            // T1 is lower triangular
                 const float ta = sm.t1[(16 * mt + li) * SM::TLD + k_nat(kk, g4)];
-                Uacc[mt][0] = mma(ta, vcur[kk * 2 + 0], Uacc[mt][0]);
-                Uacc[mt][1] = mma(ta, vcur[kk * 2 + 1], Uacc[mt][1]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) Uacc[mt][nt] = mma(ta, vcur[kk * NTL + nt], Uacc[mt][nt]);
             }
         }
         // Z = K S and U += (-T2) Z, one 16-column tile at a time
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTL; ++nt) {
             __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
             f32x4 Zacc[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Zacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk) {
-                const float sb = acc_fromc(&Sacc[0][nt], kk, 2);
+                const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     Zacc[mt] = mma(sm.k[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Zacc[mt]);
@@ -403,14 +408,14 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
         // ---- phase 5b: O = gamma o (Q S) + P U, one 16-column tile at a time
         const float* gam = sm.gate + GATE_GAM * kC;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTL; ++nt) {
             __builtin_amdgcn_sched_barrier(0);
             f32x4 Oacc[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS_DK; ++kk) {
-                const float sb = acc_fromc(&Sacc[0][nt], kk, 2);
+                const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     Oacc[mt] = mma(sm.q[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Oacc[mt]);
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
                 for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gam[16 * mt + 4 * g4 + i];
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
-                const float ub = acc_fromc(&Uacc[0][nt], kk, 2);
+                const float ub = acc_fromc(&Uacc[0][nt], kk, NTL);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (16 * (kk >> 2) > 16 * mt + 15) continue;  // P is lower triangular
@@ -445,19 +450,20 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                Sacc[mt][0][i] *= gl_last;
-                Sacc[mt][1][i] *= gl_last;
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt][i] *= gl_last;
             }
 #pragma unroll
         for (int kk = 0; kk < KS_C; ++kk) {
             const float d = kdec[k_fromc(kk, g4)];
-            const float ub0 = acc_fromc(&Uacc[0][0], kk, 2) * d;
-            const float ub1 = acc_fromc(&Uacc[0][1], kk, 2) * d;
+            float ub[NTL];
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) ub[nt] = acc_fromc(&Uacc[0][nt], kk, NTL) * d;
 #pragma unroll
             for (int mt = 0; mt < MT_S; ++mt) {
                 const float ka = sm.k[k_fromc(kk, g4) * SM::QLD + 16 * mt + li];
-                Sacc[mt][0] = mma(ka, ub0, Sacc[mt][0]);
-                Sacc[mt][1] = mma(ka, ub1, Sacc[mt][1]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = mma(ka, ub[nt], Sacc[mt][nt]);
             }
         }
 
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
+                        for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
@@ -496,25 +502,34 @@ __global__ __launch_bounds__(DV * 2) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT_S; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int SW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_v;
-    hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(blocks), dim3(DV * 2), 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<DK, DV, SW>), dim3(blocks), dim3(DV / SW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
+template <int SW>
+hipError_t launch_f32_dims(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, SW>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, SW>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, SW>(a, stream);
+    return launch_typed<64, 64, SW>(a, stream);
+}
+
+// One value head per workgroup; 16-column strips when the (sequence, value head)
+// chains do not outnumber the compute units.  Both strip widths run the same
+// arithmetic per element.
 hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128>(a, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64>(a, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128>(a, stream);
-    return launch_typed<64, 64>(a, stream);
+    if ((int64_t)a.num_seqs * a.H_v <= device_cus()) return launch_f32_dims<16>(a, stream);
+    return launch_f32_dims<32>(a, stream);
 }
 
 }  // namespace

@@ -852,6 +852,8 @@ hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
     return launch_typed<64, 64, HG, SW>(a, stream);
 }
 
+}  // namespace
+
 // Compute units of the current device (the launch goes to it), read once per device.
 int device_cus() {
     static int cus[64] = {0};
@@ -864,8 +866,6 @@ int device_cus() {
     }
     return cus[dev];
 }
-
-}  // namespace
 
 // Two value heads of a key head per workgroup share the K K^T and Q K^T tiles and
 // halve the LDS traffic of staging; one head per workgroup doubles the workgroups.

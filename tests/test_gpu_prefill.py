@@ -151,22 +151,24 @@ def test_prefill_batch_invariance():
         assert torch.equal(exp_solo[:n_i], exp_all[offs[i]:offs[i + 1]]), i
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
-def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 64),
+                                         ("f32", 128, 128), ("f32", 64, 64)])
+def test_prefill_launch_shapes_are_bitwise_equal(dtype, dk, dv):
     """With two value heads per key head the bf16 kernel gives each workgroup both
     heads when the call has enough (sequence, key head) pairs to fill the compute
     units, one head with 32-column strips when its (sequence, value head) chains
     outnumber the compute units, and one head with 16-column strips otherwise.  The
     same sequences alone (16-column strips), in a middling batch (32-column strips, one
     head) and inside a batch that fills the GPU (two heads per workgroup) give bitwise
-    equal outputs, final states and exports."""
+    equal outputs, final states and exports.  The fp32 kernel has one head per
+    workgroup and the two strip widths, chosen the same way."""
     H_k, H_v = 16, 32
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = -(-cus // H_k)                               # sequences for a full launch of head pairs
     rng = np.random.default_rng(33)
     lengths = [int(x) for x in rng.integers(1, 400, size=n)]
     lengths[0], lengths[-1] = 333, 130
-    base = W.make_workload("shape", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=lengths,
+    base = W.make_workload("shape", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths,
                            num_slots=2 * n + 4, prefill_init="slots", export_grid=64)
     dbase = to_device(base)
     exp_all, _ = run_prefill(base, dbase)
@@ -174,7 +176,7 @@ def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
     offs = binding.export_offsets(base.lengths, None, 64)
     for i in (0, n // 2, n - 1):
         a, b = int(cu[i]), int(cu[i + 1])
-        solo = W.make_workload("shape1", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=[b - a],
+        solo = W.make_workload("shape1", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype=dtype, lengths=[b - a],
                                num_slots=2 * n + 4, export_grid=64)
         for name in ("q", "k", "v", "g", "beta"):
             setattr(solo, name, getattr(base, name)[a:b].copy())
@@ -191,7 +193,7 @@ def test_prefill_launch_shapes_are_bitwise_equal(dk, dv):
     # the first m sequences: more chains than compute units, fewer head pairs
     m = cus // H_v + 1
     assert m * H_v > cus and m * H_k < cus and m < n
-    mid = W.make_workload("shape2", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype="bf16", lengths=lengths[:m],
+    mid = W.make_workload("shape2", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths[:m],
                           num_slots=2 * n + 4, export_grid=64)
     b = int(cu[m])
     for name in ("q", "k", "v", "g", "beta"):

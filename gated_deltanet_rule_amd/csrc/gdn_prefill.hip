@@ -117,7 +117,10 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
     constexpr int VPRV = DV / 4;             // 16-byte vectors per V row
     constexpr int NPV = kC * VPRV / NT;      // prefetched V vectors per thread
-    constexpr int TPW = (16 + NW - 1) / NW;  // 16x16 tiles of a 64x64 matrix per wave
+    // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row,
+    // go round robin to the waves; so do the six upper ones where they must be cleared.
+    constexpr int TPW = (10 + NW - 1) / NW;  // lower tiles per wave
+    constexpr int UPW = (6 + NW - 1) / NW;   // upper tiles per wave
     constexpr int NVF = KS_C * NTL;          // V fragments per wave
     static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         for (int kk = 0; kk < KS_C; ++kk)
 #pragma unroll
             for (int nt = 0; nt < NTL; ++nt) vcur[kk * NTL + nt] = sm.v[k_nat(kk, g4) * SM::VLD + col0 + 16 * nt + li];
-        if (wv == 0) {
+        if (wv == NW - 1) {                       // the gates, on a wave with fewer tiles
             const float gs = sm.graw[lane];
             const float bs = sm.braw[lane];
             const float Gc = dev::wave_inclusive_sum(gs);
@@ -257,9 +260,9 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
-            const int mt = t >> 2, nt = t & 3;
+            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
             f32x4 ak = {0.f, 0.f, 0.f, 0.f};
-            if (t < 16 && nt <= mt) {
+            if (t < 10) {
 #pragma unroll 2
                 for (int kk = 0; kk < KS_DK; ++kk)
                     ak = mma(sm.k[(16 * mt + li) * SM::QLD + k_nat(kk, g4)], sm.k[(16 * nt + li) * SM::QLD + k_nat(kk, g4)], ak);
@@ -270,10 +273,18 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 
         // ---- phase 2: A (zeros on and above the diagonal)
 #pragma unroll
+        for (int j = 0; j < UPW; ++j) {              // the upper tiles, cleared
+            const int u = wv + NW * j;
+            if (u >= 6) continue;
+            const int nt = 1 + (u >= 1) + (u >= 3), mt = u - (nt - 1) * nt / 2;   // (0,1) (0,2) (1,2) (0,3) ..
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.a[(16 * mt + 4 * g4 + i) * SM::ALD + 16 * nt + li] = 0.f;
+        }
+#pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
-            if (t >= 16) continue;
-            const int mt = t >> 2, nt = t & 3;
+            if (t >= 10) continue;
+            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
@@ -351,10 +362,10 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
-            if (t >= 16) continue;
-            const int mt = t >> 2, nt = t & 3;
+            if (t >= 10) continue;
+            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
             f32x4 aq = {0.f, 0.f, 0.f, 0.f};
-            if (nt <= mt) {
+            {
 #pragma unroll 2
                 for (int kk = 0; kk < KS_DK; ++kk)
                     aq = mma(sm.q[(16 * mt + li) * SM::QLD + k_nat(kk, g4)], sm.k[(16 * nt + li) * SM::QLD + k_nat(kk, g4)], aq);

@@ -33,8 +33,8 @@
 //            forward substitution (lane 16b + j owns column j of block b), then
 //            T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj column block by column block on
 //            fp32 MFMA, each T_ij overwriting A_ij (its last use)
-//   phase 4  T1 and -T2, split once per chunk into LDS (all threads)
-//   phase 5  P into LDS; U = T1 V + (-T2) Z; O = gamma o (Q S) + P U; the state
+//   phase 5  P into LDS; U = T1 V + (-T2) Z, T1 = T diag(beta) and -T2 = -T diag(beta
+//            gamma) formed from T as the products read it; O = gamma o (Q S) + P U; the state
 //            update; the grid export
 // Precision.  The MFMAs are 16x16x4 fp32 and nothing is rounded below fp32: states,
 // accumulators, gates and T's solve are fp32.  A sequence's work never
@@ -82,18 +82,15 @@ template <int DK, int DV>
 struct ScanSmem {
     static constexpr int QLD = DK + 4;        // Q and K rows (16-byte aligned, banks spread)
     static constexpr int ALD = kC + 4;        // A / T rows
-    static constexpr int TLD = kC + 4;        // T1, T2 rows
     static constexpr int PLD = kC + 4;        // P rows
     static constexpr int VLD = DV + 4;        // V rows
     float q[kC * QLD];
     float k[kC * QLD];
     union {
         float v[kC * VLD];        // V rows (staging to phase 1)
-        float a[kC * ALD];        // A, then T in place (phases 2-4)
-        float p[kC * PLD];        // then P (phase 5)
+        float a[kC * ALD];        // A, then T in place (phases 2-5)
     };
-    float t1[kC * TLD];           // T diag(beta)
-    float t2[kC * TLD];           // -T diag(beta gamma)
+    float p[kC * PLD];            // P (phase 5)
     float gate[kGates * kC];
     float graw[kC];
     float braw[kC];
@@ -344,21 +341,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         }
         dev::lds_barrier();
 
-        // ---- phase 4: T1 = T diag(beta) and -T2 = -T diag(beta gamma), all threads
-        for (int idx = tid; idx < kC * kC / 4; idx += NT) {
-            const int r = idx >> 4, s4 = (idx & 15) * 4;
-            const float4 tv = *reinterpret_cast<const float4*>(sm.a + r * SM::ALD + s4);
-            const float tr[4] = {tv.x, tv.y, tv.z, tv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = s4 + e;
-                sm.t1[r * SM::TLD + s] = tr[e] * sm.gate[GATE_BET * kC + s];
-                sm.t2[r * SM::TLD + s] = -tr[e] * sm.gate[GATE_BG * kC + s];
-            }
-        }
-        dev::lds_barrier();
-
-        // ---- phase 5a: P (into the dead A/T space); Z = K S; U = T1 V + (-T2) Z
+        // ---- phase 5a: P; Z = K S; U = T1 V + (-T2) Z with T1 = T diag(beta) and -T2 =
+        //      -T diag(beta gamma) formed from T as the products read it
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
@@ -385,7 +369,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < KS_C; ++kk) {
                 if (4 * kk > 16 * mt + 15) continue;            // T1 is lower triangular
-                const float ta = sm.t1[(16 * mt + li) * SM::TLD + k_nat(kk, g4)];
+                const float ta = sm.a[(16 * mt + li) * SM::ALD + k_nat(kk, g4)] * sm.gate[GATE_BET * kC + k_nat(kk, g4)];
 #pragma unroll
                 for (int nt = 0; nt < NTL; ++nt) Uacc[mt][nt] = mma(ta, vcur[kk * NTL + nt], Uacc[mt][nt]);
             }
@@ -410,7 +394,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (16 * (kk >> 2) > 16 * mt + 15) continue;  // T2 is lower triangular
-                    Uacc[mt][nt] = mma(sm.t2[(16 * mt + li) * SM::TLD + k_fromc(kk, g4)], zb, Uacc[mt][nt]);
+                    const float tb = -sm.a[(16 * mt + li) * SM::ALD + k_fromc(kk, g4)] * sm.gate[GATE_BG * kC + k_fromc(kk, g4)];
+                    Uacc[mt][nt] = mma(tb, zb, Uacc[mt][nt]);
                 }
             }
         }

@@ -232,7 +232,8 @@ struct Smem {
 };
 
 // Waves per SIMD the register allocation must allow: with one K buffer two workgroups
-// share a compute unit.
+// of 32-column strips share a compute unit; a workgroup of 16-column strips has one to
+// itself, two of its eight waves on each SIMD.
 template <int DV, int HG, int KB, int SW>
 constexpr int waves_per_simd() {
     return SW == 16 ? 2 : (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 > 1 ? (HG * DV / 32) * (KB == 1 ? 2 : 1) / 4 : 1;

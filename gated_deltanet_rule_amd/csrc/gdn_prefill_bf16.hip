@@ -508,7 +508,6 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
                         for (int e = 0; e < 4; ++e)
                             if (4 * r4 + e > s) acc[4 * r4 + e] = fmaf(-rows[s % 3][r4][e], t[s], acc[4 * r4 + e]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             const int bb = (0x9520 >> (4 * b)) & 15;   // blk(b, b) for b = 0..3
             unsigned short* th = reinterpret_cast<unsigned short*>(hd.sol[bb][0]);

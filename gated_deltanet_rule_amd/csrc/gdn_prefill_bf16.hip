@@ -158,6 +158,21 @@ __device__ __forceinline__ f16x4 ld4h(const _Float16* p) { return *reinterpret_c
 __device__ __forceinline__ f16x8 ld8h(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ void st4h(_Float16* p, f16x4 x) { *reinterpret_cast<f16x4*>(p) = x; }
 
+// A chunk's rows of a token-major tensor as a raw buffer: base at the chunk's first
+// row (and the head's columns), nrec bytes = the chunk's valid rows.  A load at a byte
+// offset at or past nrec returns zero without touching memory (the buffer's range
+// check), which is how rows past a partial chunk's end enter as exact zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* base, int nrec) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16_rows(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float ld4_rows(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
 // 16 g + i receives element e = 0..3 from the address of lane 16 g + 4 e + i / 4, at
 // position i % 4 of that lane's four values.  So if lane l points at row r0 + l / 4,
@@ -338,9 +353,6 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
     // product: pv[mt][nt] = V[16 mt + li][col0 + 16 nt + 4 g4 .. + 3]
     bf16x4 pv[4][NTL];
     float gpf = 0.f, bpf = 0.f;
-    auto ld16 = [](const void* base, uint32_t off) {
-        return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
-    };
     // chunk c's Q and K rows and (first wave of each head) its g and beta
     auto prefetch_qk = [&](int c, unsigned t) {
         int b0, e0;
@@ -349,23 +361,23 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
         const __bf16* qb = qg + ((size_t)tok * a.H_k + kh) * DK;
         const __bf16* kb = kg + ((size_t)tok * a.H_k + kh) * DK;
         if (!SPLIT || wv < NW / 2) {
+            const int nrec = L * a.H_k * DK * 2;   // the chunk's L rows
+            const rsrc_t rq = rows_rsrc(qb, nrec), rk = rows_rsrc(kb, nrec);
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 const unsigned i = t + NTS * j;
                 const unsigned r = i / VPR, vi = i % VPR;
                 const uint32_t off = (r * (unsigned)a.H_k * DK + vi * 8) * 2u;
-                const bool in = (int)r < L;
-                pq[j] = in ? ld16(qb, off) : make_uint4(0u, 0u, 0u, 0u);
-                pk[j] = in ? ld16(kb, off) : make_uint4(0u, 0u, 0u, 0u);
+                pq[j] = ld16_rows(rq, off);
+                pk[j] = ld16_rows(rk, off);
             }
         }
         if (lead) {
             const unsigned s = t & 63;
             const uint32_t off = (s * (unsigned)a.H_v + (unsigned)h) * 4u;
-            const char* gb = reinterpret_cast<const char*>(a.g + (size_t)tok * a.H_v);
-            const char* bb = reinterpret_cast<const char*>(a.beta + (size_t)tok * a.H_v);
-            gpf = (int)s < L ? *reinterpret_cast<const float*>(gb + off) : 0.f;
-            bpf = (int)s < L ? *reinterpret_cast<const float*>(bb + off) : 0.f;
+            const int nrec = L * a.H_v * 4;
+            gpf = ld4_rows(rows_rsrc(a.g + (size_t)tok * a.H_v, nrec), off);
+            bpf = ld4_rows(rows_rsrc(a.beta + (size_t)tok * a.H_v, nrec), off);
         }
     };
     // chunk c's V strip of this wave, straight into registers (8 bytes per lane and
@@ -374,7 +386,7 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
         int b0, e0;
         dev::chunk_span(c, off64, len, b0, e0);
         const int tok = lo + b0, L = e0 - b0;
-        const char* vb = reinterpret_cast<const char*>(vg + ((size_t)tok * a.H_v + h) * DV + col0);
+        const rsrc_t rv = rows_rsrc(vg + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 2);
         const unsigned li = (unsigned)ln & 15u, g4 = (unsigned)ln >> 4;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
             for (int nt = 0; nt < NTL; ++nt) {
                 const unsigned r = 16u * mt + li;
                 const uint32_t off = (r * (unsigned)a.H_v * DV + 16u * nt + 4u * g4) * 2u;
-                pv[mt][nt] = (int)r < L ? *reinterpret_cast<const bf16x4*>(vb + off) : bf16x4{};
+                pv[mt][nt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off, 0, 0));
             }
     };
     // Write chunk c's prefetched Q rows and gates (by chunk parity) to LDS.  For chunk

@@ -75,6 +75,17 @@ __device__ __forceinline__ float acc_fromc(const f32x4* tiles, int ks, int strid
     return tiles[(ks >> 2) * stride][ks & 3];
 }
 
+// A chunk's rows of a token-major tensor as a raw buffer of nrec bytes (the chunk's
+// valid rows): a load at a byte offset at or past nrec returns zero without touching
+// memory (the buffer's range check), so rows past a partial chunk's end enter as zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* base, int nrec) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16_rows(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 constexpr int kGates = 5;
 enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_BG = 3, GATE_KDEC = 4 };
 
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     constexpr int TPW = (10 + NW - 1) / NW;  // lower tiles per wave
     constexpr int UPW = (6 + NW - 1) / NW;   // upper tiles per wave
     constexpr int NVF = KS_C * NTL;          // V fragments per wave
-    static_assert(NPF * NT == 2 * kC * VPR, "Q/K prefetch must divide evenly");
+    static_assert(NPF * NT == 2 * kC * VPR && (kC * VPR) % NT == 0, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
 
@@ -169,32 +180,28 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     uint4 pf[NPF];
     uint4 pv[NPV];
     float gbpf = 0.f;
-    // load 16 bytes at a uniform base plus an unsigned 32-bit byte offset (the
-    // scalar-base + vector-offset form of the global load)
-    auto ld16 = [](const void* base, uint32_t off) {
-        return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
-    };
     auto prefetch = [&](int c, int t) {
         int b0, e0;
         dev::chunk_span(c, off64, len, b0, e0);
         const int tok = lo + b0, L = e0 - b0;
-        const float* qb = qg + (size_t)tok * a.H_k * DK;
-        const float* kb = kg + (size_t)tok * a.H_k * DK;
-        const float* vb = vg + (size_t)tok * a.H_v * DV;
+        // the chunk's rows as raw buffers: loads past its L rows return zeros
+        const rsrc_t rq = rows_rsrc(qg + (size_t)tok * a.H_k * DK, L * a.H_k * DK * 4);
+        const rsrc_t rk = rows_rsrc(kg + (size_t)tok * a.H_k * DK, L * a.H_k * DK * 4);
+        const rsrc_t rv = rows_rsrc(vg + (size_t)tok * a.H_v * DV, L * a.H_v * DV * 4);
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
             const int i = t + NT * j;
-            const int which = i / (kC * VPR);            // 0: Q, 1: K
+            const int which = NT * j / (kC * VPR);       // 0: Q, 1: K (uniform: NT divides kC VPR)
             const int r = (i / VPR) % kC, vi = i % VPR;
             const uint32_t off = (uint32_t)((r * a.H_k + kh) * DK + vi * 4) * 4u;
-            pf[j] = r < L ? ld16(which == 0 ? qb : kb, off) : make_uint4(0u, 0u, 0u, 0u);
+            pf[j] = ld16_rows(which == 0 ? rq : rk, off);
         }
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
             const int i = t + NT * j;
             const int r = i / VPRV, vi = i % VPRV;
             const uint32_t off = (uint32_t)((r * a.H_v + h) * DV + vi * 4) * 4u;
-            pv[j] = r < L ? ld16(vb, off) : make_uint4(0u, 0u, 0u, 0u);
+            pv[j] = ld16_rows(rv, off);
         }
         if (t < 2 * kC) {                                 // g then beta of this head
             const int which = t / kC, s = t % kC;

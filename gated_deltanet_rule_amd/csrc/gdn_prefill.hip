@@ -309,13 +309,15 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
             {
                 const int b = g4, j = li;
                 const float* Ab = as + (16 * b) * ALD + 16 * b;
+                // each row starts from column j of I: rows above j then sum products
+                // with zeros only (t = 0 there), row j comes out as 1
                 float t[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float acc = 0.f;
+                    float acc = r == j ? 1.f : 0.f;
 #pragma unroll
                     for (int s = 0; s < r; ++s) acc = fmaf(-Ab[r * ALD + s], t[s], acc);
-                    t[r] = r < j ? 0.f : (r == j ? 1.f : acc);
+                    t[r] = acc;
                 }
                 __builtin_amdgcn_wave_barrier();
                 float* Tb = as + (16 * b) * ALD + 16 * b;

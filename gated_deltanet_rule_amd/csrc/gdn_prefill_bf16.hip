@@ -496,9 +496,11 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
             }
             const int b = g4, jc = li;
             const float* AT = hd.at + b * SM::ATB;
+            // acc starts as column jc of I: t[s] = acc[s] is then 0 above the diagonal
+            // (every product added there is 0 x A), 1 on it and the substitution below
             float acc[16], t[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[r] = r == jc ? 1.f : 0.f;
             // row s of the transposed block holds A[r][s] at column r; rows are read two
             // steps before they are used, so the LDS latency overlaps the arithmetic
             f32x4 rows[3][4];
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 if (s + 2 < 15) load_row(s + 2);
-                t[s] = s < jc ? 0.f : (s == jc ? 1.f : acc[s]);
+                t[s] = acc[s];
                 if (s < 15) {
 #pragma unroll
                     for (int r4 = (s + 1) / 4; r4 < 4; ++r4)

@@ -13,31 +13,32 @@
 // chunked WY/UT form:
 //     G   = inclusive cumsum of g inside the chunk,  gamma = e^G
 //     A   = strictly lower part of diag(beta) (K K^T) o D,   D[r][s] = e^(G_r - G_s)
-//     T   = (I + A)^-1
-//     T1  = T diag(beta),   T2 = T diag(beta gamma)
-//     U   = T1 V - T2 (K S0)                       (= U~ - W S0 with W = T2 K)
+//     R   = diag(beta) (V - diag(gamma) K S0)
+//     U   = (I + A)^-1 R                           (a unit lower-triangular solve)
 //     O   = scale (diag(gamma) Q S0 + (Q K^T o D o lower-incl-diagonal) U)
 //     S1  = gamma_last S0 + K^T (diag(e^(G_last - G)) U)
+// The solve runs on 16-row blocks: with N = -A and T_ii = (I + A_ii)^-1 (16 x 16),
+//     U_i = T_ii (R_i + sum_{j<i} N_ij U_j).
 //
 // One kernel.  A workgroup owns one sequence and one value head and walks the
 // sequence's chunks in order.  Per value head, d_v is split into 32-column
-// strips, one wave each; a wave keeps its strip of S (d_k x 32, fp32) in MFMA
-// accumulator registers for the whole sequence.  The d_v columns of S, U and O are
+// strips (16-column ones when the call has no more chains than compute units), one
+// wave each; a wave keeps its strip of S (d_k x 32 or d_k x 16, fp32) in MFMA
+// accumulator registers for the whole sequence.  The d_v columns of S, R, U and O are
 // independent, so strips never exchange data.  Per chunk:
-//   load     Q and K rows from the registers they were
-//            prefetched into during the previous chunk; V fragments likewise
-//   phase 1  gates by a wave scan; K K^T and Q K^T (lower tiles) and Z = K S for
-//            each strip, on MFMA
-//   phase 2  A for each head into LDS (fp32)
-//   phase 3  T = (I + A)^-1 in place, one wave per head: the 16x16 diagonal blocks by
-//            forward substitution (lane 16b + j owns column j of block b), then
-//            T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj column block by column block on
-//            fp32 MFMA, each T_ij overwriting A_ij (its last use)
-//   phase 5  P into LDS; U = T1 V + (-T2) Z, T1 = T diag(beta) and -T2 = -T diag(beta
-//            gamma) formed from T as the products read it; O = gamma o (Q S) + P U; the state
-//            update; the grid export
+//   stage    Q, K, V rows and the raw gates from the registers they were prefetched
+//            into during the previous chunk, into LDS
+//   phase 1  each wave's V strip into registers; gates by a wave scan; the K K^T
+//            lower tiles on MFMA, round robin over the waves
+//   phase 2  N = -A into LDS (fp32)
+//   phase 3  the first wave inverts the four diagonal blocks by forward substitution
+//            (lane 16b + j owns column j of block b); the other waves form the P
+//            tiles; then every wave forms Z = K S and R for its strip
+//   phase 4  per strip: the block solve for U on MFMA, X_i's accumulator feeding the
+//            products directly; O = gamma o (Q S) + P U; the state update; the grid
+//            export
 // Precision.  The MFMAs are 16x16x4 fp32 and nothing is rounded below fp32: states,
-// accumulators, gates and T's solve are fp32.  A sequence's work never
+// accumulators, gates and the diagonal inverses are fp32.  A sequence's work never
 // depends on the other sequences of the call, so its results are bitwise
 // independent of its batch-mates; the chunks lie on the absolute 64-token grid, so
 // a resume from an exported grid state continues with the same arithmetic.
@@ -86,8 +87,8 @@ __device__ __forceinline__ uint4 ld16_rows(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-constexpr int kGates = 5;
-enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_BG = 3, GATE_KDEC = 4 };
+constexpr int kGates = 4;
+enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3 };
 
 template <int DK, int DV>
 struct ScanSmem {
@@ -99,9 +100,9 @@ struct ScanSmem {
     float k[kC * QLD];
     union {
         float v[kC * VLD];        // V rows (staging to phase 1)
-        float a[kC * ALD];        // A, then T in place (phases 2-5)
+        float a[kC * ALD];        // N = -A, then T_bb in place of N_bb (phases 2-4)
     };
-    float p[kC * PLD];            // P (phase 5)
+    float p[kC * PLD];            // P (phases 3-4)
     float gate[kGates * kC];
     float graw[kC];
     float braw[kC];
@@ -126,10 +127,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     constexpr int VPRV = DV / 4;             // 16-byte vectors per V row
     constexpr int NPV = kC * VPRV / NT;      // prefetched V vectors per thread
     // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row,
-    // go round robin to the waves; so do the six upper ones where they must be cleared.
+    // go round robin to the waves.
     constexpr int TPW = (10 + NW - 1) / NW;  // lower tiles per wave
-    constexpr int UPW = (6 + NW - 1) / NW;   // upper tiles per wave
-    constexpr int NVF = KS_C * NTL;          // V fragments per wave
     static_assert(NPF * NT == 2 * kC * VPR && (kC * VPR) % NT == 0, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
@@ -242,22 +241,24 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         // the staged inputs are in LDS: fetch the next chunk's behind this chunk's compute
         if (c + 1 < nchunks) prefetch(c + 1, tid_l);
 
-        // ---- phase 1: this wave's V fragments; gates; K K^T lower tiles
-        float vcur[NVF];
+        // ---- phase 1: this wave's V strip in the accumulator layout; gates; K K^T
+        //      lower tiles
+        f32x4 Racc[4][NTL];          // V, then R = beta (V - gamma Z), then X_i of the solve
 #pragma unroll
-        for (int kk = 0; kk < KS_C; ++kk)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) vcur[kk * NTL + nt] = sm.v[k_nat(kk, g4) * SM::VLD + col0 + 16 * nt + li];
+            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Racc[mt][nt][i] = sm.v[(16 * mt + 4 * g4 + i) * SM::VLD + col0 + 16 * nt + li];
         if (wv == NW - 1) {                       // the gates, on a wave with fewer tiles
             const float gs = sm.graw[lane];
             const float bs = sm.braw[lane];
             const float Gc = dev::wave_inclusive_sum(gs);
             const float G_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gc), kC - 1));
-            const float gam = expf(Gc);
             sm.gate[GATE_G * kC + lane] = Gc;
-            sm.gate[GATE_GAM * kC + lane] = gam;
+            sm.gate[GATE_GAM * kC + lane] = expf(Gc);
             sm.gate[GATE_BET * kC + lane] = bs;
-            sm.gate[GATE_BG * kC + lane] = bs * gam;
             sm.gate[GATE_KDEC * kC + lane] = expf(G_last - Gc);
         }
         f32x4 kkt[TPW];
@@ -275,15 +276,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         }
         dev::lds_barrier();
 
-        // ---- phase 2: A (zeros on and above the diagonal)
-#pragma unroll
-        for (int j = 0; j < UPW; ++j) {              // the upper tiles, cleared
-            const int u = wv + NW * j;
-            if (u >= 6) continue;
-            const int nt = 1 + (u >= 1) + (u >= 3), mt = u - (nt - 1) * nt / 2;   // (0,1) (0,2) (1,2) (0,3) ..
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.a[(16 * mt + 4 * g4 + i) * SM::ALD + 16 * nt + li] = 0.f;
-        }
+        // ---- phase 2: N = -A on the ten lower tiles (zeros on and above the diagonal);
+        //      nothing reads the upper tiles
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
@@ -292,98 +286,56 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                sm.a[r * SM::ALD + s] = s < r ? sm.gate[GATE_BET * kC + r] * kkt[j][i] *
-                                                    expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s])
+                sm.a[r * SM::ALD + s] = s < r ? -(sm.gate[GATE_BET * kC + r] * kkt[j][i] *
+                                                  expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]))
                                               : 0.f;
             }
         }
         dev::lds_barrier();
 
-        // ---- phase 3: T = (I + A)^-1 in place, the first wave: the 16x16 diagonal blocks
-        //      by forward substitution (lane 16 b + j owns column j of block b), then
-        //      T_ij = -T_ii sum_{k=j..i-1} A_ik T_kj column block by column block,
-        //      each T_ij overwriting A_ij (its last use)
+        // ---- phase 3: the first wave inverts the diagonal blocks, T_bb = (I + A_bb)^-1 in
+        //      place of N_bb, by forward substitution (lane 16 b + j owns column j of
+        //      block b); the other waves (all of them when there are fewer than four)
+        //      form P = Q K^T o D, lower tiles; then every wave forms Z = K S and
+        //      R = beta (V - gamma Z) for its strip
         if (wv == 0) {
-            float* as = sm.a;
-            constexpr int ALD = SM::ALD;
-            {
-                const int b = g4, j = li;
-                const float* Ab = as + (16 * b) * ALD + 16 * b;
-                // each row starts from column j of I: rows above j then sum products
-                // with zeros only (t = 0 there), row j comes out as 1
-                float t[16];
+            const int b = g4, j = li;
+            const float* Nb = sm.a + (16 * b) * SM::ALD + 16 * b;
+            // each row starts from column j of I: rows above j then sum products with
+            // zeros only (t = 0 there), row j comes out as 1
+            float t[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = r == j ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == j ? 1.f : 0.f;
 #pragma unroll
-                    for (int s = 0; s < r; ++s) acc = fmaf(-Ab[r * ALD + s], t[s], acc);
-                    t[r] = acc;
-                }
-                __builtin_amdgcn_wave_barrier();
-                float* Tb = as + (16 * b) * ALD + 16 * b;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Tb[r * ALD + j] = t[r];
+                for (int s = 0; s < r; ++s) acc = fmaf(Nb[r * SM::ALD + s], t[s], acc);
+                t[r] = acc;
             }
             __builtin_amdgcn_wave_barrier();
+            float* Tb = sm.a + (16 * b) * SM::ALD + 16 * b;
 #pragma unroll
-            for (int jb = 0; jb < 3; ++jb) {
-#pragma unroll
-                for (int ib = jb + 1; ib < 4; ++ib) {
-                    f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = jb; kb < ib; ++kb)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            X = mma(as[(16 * ib + li) * ALD + 16 * kb + 4 * q + g4],    // A_ik[m][4q + g]
-                                    as[(16 * kb + 4 * q + g4) * ALD + 16 * jb + li],    // T_kj[4q + g][n]
-                                    X);
-                    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)   // B from X's registers: element q is row 4g + q
-                        Y = mma(as[(16 * ib + li) * ALD + 16 * ib + 4 * g4 + q], X[q], Y);
-                    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) as[(16 * ib + 4 * g4 + i) * ALD + 16 * jb + li] = -Y[i];
-                    __builtin_amdgcn_wave_barrier();
-                }
-            }
+            for (int r = 0; r < 16; ++r) Tb[r * SM::ALD + j] = t[r];
         }
-        dev::lds_barrier();
-
-        // ---- phase 5a: P; Z = K S; U = T1 V + (-T2) Z with T1 = T diag(beta) and -T2 =
-        //      -T diag(beta gamma) formed from T as the products read it
+        constexpr int PW0 = NW >= 4 ? 1 : 0;      // the first P wave
+        constexpr int PPW = (10 + (NW - PW0) - 1) / (NW - PW0);   // P tiles per wave
+        if (wv >= PW0) {
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int t = wv + NW * j;
-            if (t >= 10) continue;
-            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-            f32x4 aq = {0.f, 0.f, 0.f, 0.f};
-            {
+            for (int j = 0; j < PPW; ++j) {
+                const int t = (wv - PW0) + (NW - PW0) * j;
+                if (t >= 10) continue;
+                const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
+                f32x4 aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
                 for (int kk = 0; kk < KS_DK; ++kk)
                     aq = mma(sm.q[(16 * mt + li) * SM::QLD + k_nat(kk, g4)], sm.k[(16 * nt + li) * SM::QLD + k_nat(kk, g4)], aq);
-            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                sm.p[r * SM::PLD + s] = s <= r ? aq[i] * expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]) : 0.f;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 Uacc[4][NTL];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) Uacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS_C; ++kk) {
-                if (4 * kk > 16 * mt + 15) continue;            // T1 is lower triangular
-                const float ta = sm.a[(16 * mt + li) * SM::ALD + k_nat(kk, g4)] * sm.gate[GATE_BET * kC + k_nat(kk, g4)];
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Uacc[mt][nt] = mma(ta, vcur[kk * NTL + nt], Uacc[mt][nt]);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
+                    sm.p[r * SM::PLD + s] = s <= r ? aq[i] * expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]) : 0.f;
+                }
             }
         }
-        // Z = K S and U += (-T2) Z, one 16-column tile at a time
+        // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
             __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
@@ -398,19 +350,39 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
                     Zacc[mt] = mma(sm.k[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Zacc[mt]);
             }
 #pragma unroll
-            for (int kk = 0; kk < KS_C; ++kk) {
-                const float zb = acc_fromc(&Zacc[0], kk, 1);
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 gam = *reinterpret_cast<const f32x4*>(sm.gate + GATE_GAM * kC + 16 * mt + 4 * g4);
+                const f32x4 bet = *reinterpret_cast<const f32x4*>(sm.gate + GATE_BET * kC + 16 * mt + 4 * g4);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    if (16 * (kk >> 2) > 16 * mt + 15) continue;  // T2 is lower triangular
-                    const float tb = -sm.a[(16 * mt + li) * SM::ALD + k_fromc(kk, g4)] * sm.gate[GATE_BG * kC + k_fromc(kk, g4)];
-                    Uacc[mt][nt] = mma(tb, zb, Uacc[mt][nt]);
-                }
+                for (int i = 0; i < 4; ++i) Racc[mt][nt][i] = bet[i] * fmaf(-gam[i], Zacc[mt][i], Racc[mt][nt][i]);
             }
         }
-        dev::lds_barrier();   // P is complete
+        dev::lds_barrier();   // the T_bb and P are complete
 
-        // ---- phase 5b: O = gamma o (Q S) + P U, one 16-column tile at a time
+        // ---- phase 4: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
+        //      right-looking: once U_i exists it enters every later X_k.  X_i's
+        //      accumulator feeds the products as their B operand (from-C order).
+        f32x4 Uacc[4][NTL];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    u = mma(sm.a[(16 * i + li) * SM::ALD + 16 * i + 4 * g4 + kk], Racc[i][nt][kk], u);
+                Uacc[i][nt] = u;
+            }
+#pragma unroll
+            for (int k = i + 1; k < 4; ++k)
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        Racc[k][nt] = mma(sm.a[(16 * k + li) * SM::ALD + 16 * i + 4 * g4 + kk], Uacc[i][nt][kk], Racc[k][nt]);
+        }
+
+        // ---- O = gamma o (Q S) + P U, one 16-column tile at a time
         const float* gam = sm.gate + GATE_GAM * kC;
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
@@ -448,7 +420,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         }
 
         __builtin_amdgcn_sched_barrier(0);
-        // ---- phase 5c: S = gamma_last S + K^T (diag(e^(G_last - G)) U)
+        // ---- S = gamma_last S + K^T (diag(e^(G_last - G)) U)
         const float gl_last = gam[kC - 1];
         const float* kdec = sm.gate + GATE_KDEC * kC;
 #pragma unroll

@@ -61,7 +61,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // B[k][l % 16] for one k per step; the C/D tile is held as C[4 (l / 16) + i][l % 16],
 // i = 0..3.  Which k a lane stands for only has to agree between A and B, so two k
 // orders are used:
-//   natural   lane group g holds k = 4 ks + g
+//   blocked   lane group g holds the contiguous k = (K / 4) g .. (K / 4) g + K / 4 - 1,
+//             for products of two row-major LDS operands (16-byte reads)
 //   from-C    the order in which a C tile's registers already sit, so that an fp32
 //             accumulator tile can feed the next product as its B operand without an
 //             LDS round trip: step ks is register (ks & 3) of C tile (ks >> 2), i.e.
@@ -69,11 +70,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ int k_nat(int ks, int g) { return 4 * ks + g; }
 __device__ __forceinline__ int k_fromc(int ks, int g) { return 16 * (ks >> 2) + 4 * g + (ks & 3); }
 // element k of a C-layout tile set (tiles[t * stride] holds rows 16 t ..), from-C order
 __device__ __forceinline__ float acc_fromc(const f32x4* tiles, int ks, int stride) {
     return tiles[(ks >> 2) * stride][ks & 3];
+}
+// The 16x16 tile X Y^T of two row blocks of K columns in LDS (ra, rb: this lane's row
+// of each), k in blocked order: every operand arrives in 16-byte reads issued ahead of
+// the products.
+template <int K>
+__device__ __forceinline__ f32x4 row_tile(const float* ra, const float* rb, int g) {
+    f32x4 xa[K / 16], xb[K / 16];
+#pragma unroll
+    for (int q = 0; q < K / 16; ++q) {
+        xa[q] = *reinterpret_cast<const f32x4*>(ra + (K / 4) * g + 4 * q);
+        xb[q] = *reinterpret_cast<const f32x4*>(rb + (K / 4) * g + 4 * q);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < K / 16; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mma(xa[q][e], xb[q][e], acc);
+    return acc;
 }
 
 // A chunk's rows of a token-major tensor as a raw buffer of nrec bytes (the chunk's
@@ -266,13 +284,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
             const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-            f32x4 ak = {0.f, 0.f, 0.f, 0.f};
-            if (t < 10) {
-#pragma unroll 2
-                for (int kk = 0; kk < KS_DK; ++kk)
-                    ak = mma(sm.k[(16 * mt + li) * SM::QLD + k_nat(kk, g4)], sm.k[(16 * nt + li) * SM::QLD + k_nat(kk, g4)], ak);
-            }
-            kkt[j] = ak;
+            kkt[j] = t < 10 ? row_tile<DK>(sm.k + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         dev::lds_barrier();
 
@@ -324,10 +337,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
                 const int t = (wv - PW0) + (NW - PW0) * j;
                 if (t >= 10) continue;
                 const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-                f32x4 aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-                for (int kk = 0; kk < KS_DK; ++kk)
-                    aq = mma(sm.q[(16 * mt + li) * SM::QLD + k_nat(kk, g4)], sm.k[(16 * nt + li) * SM::QLD + k_nat(kk, g4)], aq);
+                const f32x4 aq = row_tile<DK>(sm.q + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;

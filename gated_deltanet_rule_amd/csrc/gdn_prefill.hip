@@ -28,13 +28,13 @@
 // independent, so strips never exchange data.  Per chunk:
 //   stage    Q, K, V rows and the raw gates from the registers they were prefetched
 //            into during the previous chunk, into LDS
-//   phase 1  each wave's V strip into registers; gates by a wave scan; the K K^T
-//            lower tiles on MFMA, round robin over the waves
-//   phase 2  N = -A into LDS (fp32)
-//   phase 3  the first wave inverts the four diagonal blocks by forward substitution
-//            (lane 16b + j owns column j of block b); the other waves form the P
-//            tiles; then every wave forms Z = K S and R for its strip
-//   phase 4  per strip: the block solve for U on MFMA, X_i's accumulator feeding the
+//   phase 1  each wave's V strip into registers; the gates by a wave scan (every
+//            wave, the same table); the K K^T lower tiles on MFMA, round robin over
+//            the waves, each written out as N = -A into LDS (fp32)
+//   phase 2  the first wave inverts the four diagonal blocks by forward substitution
+//            (lane 16b + j owns column j of block b); the waves form the P tiles
+//            (the first one fewer); then every wave forms Z = K S and R for its strip
+//   phase 3  per strip: the block solve for U on MFMA, X_i's accumulator feeding the
 //            products directly; O = gamma o (Q S) + P U; the state update; the grid
 //            export
 // Precision.  The MFMAs are 16x16x4 fp32 and nothing is rounded below fp32: states,
@@ -75,6 +75,17 @@ __device__ __forceinline__ int k_fromc(int ks, int g) { return 16 * (ks >> 2) + 
 __device__ __forceinline__ float acc_fromc(const f32x4* tiles, int ks, int stride) {
     return tiles[(ks >> 2) * stride][ks & 3];
 }
+// P tile j of wave wv (10 or more: none).  With more than two waves, the waves after
+// the first take the first NW - 1 tiles, the first wave (which also inverts the
+// diagonal blocks) the next one, and the rest go round robin over the waves after the
+// first; with two, plain round robin.
+template <int NW>
+__device__ __forceinline__ int p_tile(int wv, int j) {
+    if (NW <= 2) return wv + NW * j;
+    if (wv == 0) return j == 0 ? NW - 1 : 10;
+    return j == 0 ? wv - 1 : NW + (j - 1) * (NW - 1) + (wv - 1);
+}
+
 // The 16x16 tile X Y^T of two row blocks of K columns in LDS (ra, rb: this lane's row
 // of each), k in blocked order: every operand arrives in 16-byte reads issued ahead of
 // the products.
@@ -116,11 +127,9 @@ struct ScanSmem {
     static constexpr int VLD = DV + 4;        // V rows
     float q[kC * QLD];
     float k[kC * QLD];
-    union {
-        float v[kC * VLD];        // V rows (staging to phase 1)
-        float a[kC * ALD];        // N = -A, then T_bb in place of N_bb (phases 2-4)
-    };
-    float p[kC * PLD];            // P (phases 3-4)
+    float v[kC * VLD];            // V rows (staging to phase 1)
+    float a[kC * ALD];            // N = -A, then T_bb in place of N_bb (phases 1-3)
+    float p[kC * PLD];            // P (phases 2-3)
     float gate[kGates * kC];
     float graw[kC];
     float braw[kC];
@@ -144,9 +153,10 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
     constexpr int VPRV = DV / 4;             // 16-byte vectors per V row
     constexpr int NPV = kC * VPRV / NT;      // prefetched V vectors per thread
-    // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row,
-    // go round robin to the waves.
-    constexpr int TPW = (10 + NW - 1) / NW;  // lower tiles per wave
+    // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row:
+    // the K K^T ones go round robin to the waves, the P ones as p_tile deals them.
+    constexpr int TPW = (10 + NW - 1) / NW;  // K K^T tiles per wave
+    constexpr int PPW = NW <= 2 ? (10 + NW - 1) / NW : 1 + (10 - NW + NW - 2) / (NW - 1);   // P tiles
     static_assert(NPF * NT == 2 * kC * VPR && (kC * VPR) % NT == 0, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
@@ -259,8 +269,11 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         // the staged inputs are in LDS: fetch the next chunk's behind this chunk's compute
         if (c + 1 < nchunks) prefetch(c + 1, tid_l);
 
-        // ---- phase 1: this wave's V strip in the accumulator layout; gates; K K^T
-        //      lower tiles
+        // ---- phase 1: this wave's V strip in the accumulator layout; the gates (every
+        //      wave scans them and writes the same table, so that none waits for
+        //      another); the K K^T lower tiles, round robin, each written out as
+        //      N = -A at once (zeros on and above the diagonal; nothing reads the upper
+        //      tiles)
         f32x4 Racc[4][NTL];          // V, then R = beta (V - gamma Z), then X_i of the solve
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     Racc[mt][nt][i] = sm.v[(16 * mt + 4 * g4 + i) * SM::VLD + col0 + 16 * nt + li];
-        if (wv == NW - 1) {                       // the gates, on a wave with fewer tiles
+        {
             const float gs = sm.graw[lane];
             const float bs = sm.braw[lane];
             const float Gc = dev::wave_inclusive_sum(gs);
@@ -279,37 +292,27 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
             sm.gate[GATE_BET * kC + lane] = bs;
             sm.gate[GATE_KDEC * kC + lane] = expf(G_last - Gc);
         }
-        f32x4 kkt[TPW];
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int t = wv + NW * j;
-            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-            kkt[j] = t < 10 ? row_tile<DK>(sm.k + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        dev::lds_barrier();
-
-        // ---- phase 2: N = -A on the ten lower tiles (zeros on and above the diagonal);
-        //      nothing reads the upper tiles
+        __builtin_amdgcn_wave_barrier();   // the table is written before any lane reads it
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int t = wv + NW * j;
             if (t >= 10) continue;
             const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
+            const f32x4 kk = row_tile<DK>(sm.k + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                sm.a[r * SM::ALD + s] = s < r ? -(sm.gate[GATE_BET * kC + r] * kkt[j][i] *
+                sm.a[r * SM::ALD + s] = s < r ? -(sm.gate[GATE_BET * kC + r] * kk[i] *
                                                   expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]))
                                               : 0.f;
             }
         }
-        dev::lds_barrier();
+        dev::lds_barrier();   // N is complete
 
-        // ---- phase 3: the first wave inverts the diagonal blocks, T_bb = (I + A_bb)^-1 in
+        // ---- phase 2: the first wave inverts the diagonal blocks, T_bb = (I + A_bb)^-1 in
         //      place of N_bb, by forward substitution (lane 16 b + j owns column j of
-        //      block b); the other waves (all of them when there are fewer than four)
-        //      form P = Q K^T o D, lower tiles; then every wave forms Z = K S and
+        //      block b), and forms one P tile; the other waves form the other P tiles
+        //      (P = Q K^T o D, lower tiles); then every wave forms Z = K S and
         //      R = beta (V - gamma Z) for its strip
         if (wv == 0) {
             const int b = g4, j = li;
@@ -329,20 +332,16 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) Tb[r * SM::ALD + j] = t[r];
         }
-        constexpr int PW0 = NW >= 4 ? 1 : 0;      // the first P wave
-        constexpr int PPW = (10 + (NW - PW0) - 1) / (NW - PW0);   // P tiles per wave
-        if (wv >= PW0) {
 #pragma unroll
-            for (int j = 0; j < PPW; ++j) {
-                const int t = (wv - PW0) + (NW - PW0) * j;
-                if (t >= 10) continue;
-                const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-                const f32x4 aq = row_tile<DK>(sm.q + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
+        for (int j = 0; j < PPW; ++j) {
+            const int t = p_tile<NW>(wv, j);
+            if (t >= 10) continue;
+            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
+            const f32x4 aq = row_tile<DK>(sm.q + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                    sm.p[r * SM::PLD + s] = s <= r ? aq[i] * expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]) : 0.f;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
+                sm.p[r * SM::PLD + s] = s <= r ? aq[i] * expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]) : 0.f;
             }
         }
         // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
@@ -369,7 +368,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         }
         dev::lds_barrier();   // the T_bb and P are complete
 
-        // ---- phase 4: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
+        // ---- phase 3: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
         //      right-looking: once U_i exists it enters every later X_k.  X_i's
         //      accumulator feeds the products as their B operand (from-C order).
         f32x4 Uacc[4][NTL];

@@ -29,11 +29,11 @@
 //   stage    Q, K, V rows and the raw gates from the registers they were prefetched
 //            into during the previous chunk, into LDS
 //   phase 1  each wave's V strip into registers; the gates by a wave scan (every
-//            wave, the same table); the K K^T lower tiles on MFMA, round robin over
-//            the waves, each written out as N = -A into LDS (fp32)
+//            wave, the same table); the lower tiles of K K^T and Q K^T on MFMA, round
+//            robin over the waves, written out as N = -A and P into LDS (fp32)
 //   phase 2  the first wave inverts the four diagonal blocks by forward substitution
-//            (lane 16b + j owns column j of block b); the waves form the P tiles
-//            (the first one fewer); then every wave forms Z = K S and R for its strip
+//            (lane 16b + j owns column j of block b); every wave forms Z = K S and R
+//            for its strip
 //   phase 3  per strip: the block solve for U on MFMA, X_i's accumulator feeding the
 //            products directly; O = gamma o (Q S) + P U; the state update; the grid
 //            export
@@ -75,17 +75,6 @@ __device__ __forceinline__ int k_fromc(int ks, int g) { return 16 * (ks >> 2) + 
 __device__ __forceinline__ float acc_fromc(const f32x4* tiles, int ks, int stride) {
     return tiles[(ks >> 2) * stride][ks & 3];
 }
-// P tile j of wave wv (10 or more: none).  With more than two waves, the waves after
-// the first take the first NW - 1 tiles, the first wave (which also inverts the
-// diagonal blocks) the next one, and the rest go round robin over the waves after the
-// first; with two, plain round robin.
-template <int NW>
-__device__ __forceinline__ int p_tile(int wv, int j) {
-    if (NW <= 2) return wv + NW * j;
-    if (wv == 0) return j == 0 ? NW - 1 : 10;
-    return j == 0 ? wv - 1 : NW + (j - 1) * (NW - 1) + (wv - 1);
-}
-
 // The 16x16 tile X Y^T of two row blocks of K columns in LDS (ra, rb: this lane's row
 // of each), k in blocked order: every operand arrives in 16-byte reads issued ahead of
 // the products.
@@ -116,20 +105,22 @@ __device__ __forceinline__ uint4 ld16_rows(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-constexpr int kGates = 4;
-enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3 };
+// Per-token gate rows of a chunk: G (inclusive cumsum of g), gamma = e^G, beta,
+// e^(G_last - G), -beta and 1 (the row factors of the N and the P tiles).
+constexpr int kGates = 6;
+enum { GATE_G = 0, GATE_GAM = 1, GATE_BET = 2, GATE_KDEC = 3, GATE_NBET = 4, GATE_ONE = 5 };
 
 template <int DK, int DV>
 struct ScanSmem {
     static constexpr int QLD = DK + 4;        // Q and K rows (16-byte aligned, banks spread)
     static constexpr int ALD = kC + 4;        // A / T rows
-    static constexpr int PLD = kC + 4;        // P rows
+    static constexpr int PLD = ALD;           // P rows (the same pitch: tiles of either)
     static constexpr int VLD = DV + 4;        // V rows
     float q[kC * QLD];
     float k[kC * QLD];
     float v[kC * VLD];            // V rows (staging to phase 1)
     float a[kC * ALD];            // N = -A, then T_bb in place of N_bb (phases 1-3)
-    float p[kC * PLD];            // P (phases 2-3)
+    float p[kC * PLD];            // P (phases 1-3)
     float gate[kGates * kC];
     float graw[kC];
     float braw[kC];
@@ -153,10 +144,9 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     constexpr int NPF = 2 * kC * VPR / NT;   // prefetched Q/K vectors per thread
     constexpr int VPRV = DV / 4;             // 16-byte vectors per V row
     constexpr int NPV = kC * VPRV / NT;      // prefetched V vectors per thread
-    // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row:
-    // the K K^T ones go round robin to the waves, the P ones as p_tile deals them.
-    constexpr int TPW = (10 + NW - 1) / NW;  // K K^T tiles per wave
-    constexpr int PPW = NW <= 2 ? (10 + NW - 1) / NW : 1 + (10 - NW + NW - 2) / (NW - 1);   // P tiles
+    // The ten lower 16x16 tiles (mt, nt), nt <= mt, of a 64x64 matrix, numbered row by row,
+    // of K K^T and then of Q K^T go round robin to the waves.
+    constexpr int TPW = (20 + NW - 1) / NW;  // tiles per wave
     static_assert(NPF * NT == 2 * kC * VPR && (kC * VPR) % NT == 0, "Q/K prefetch must divide evenly");
     static_assert(NPV * NT == kC * VPRV, "V prefetch must divide evenly");
     __shared__ __attribute__((aligned(16))) SM sm;
@@ -166,7 +156,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     const int h = blockIdx.x - seq * a.H_v;
     const int kh = h / G;
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
     int lane = tid & 63;
     const int col0 = SW * wv;
 
@@ -271,9 +261,9 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 
         // ---- phase 1: this wave's V strip in the accumulator layout; the gates (every
         //      wave scans them and writes the same table, so that none waits for
-        //      another); the K K^T lower tiles, round robin, each written out as
-        //      N = -A at once (zeros on and above the diagonal; nothing reads the upper
-        //      tiles)
+        //      another); the twenty tiles, the ten lower ones of K K^T (each written out
+        //      as N = -A at once, zeros on and above the diagonal; nothing reads the
+        //      upper tiles) and then the ten of P = Q K^T o D, round robin
         f32x4 Racc[4][NTL];          // V, then R = beta (V - gamma Z), then X_i of the solve
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -290,30 +280,45 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
             sm.gate[GATE_G * kC + lane] = Gc;
             sm.gate[GATE_GAM * kC + lane] = expf(Gc);
             sm.gate[GATE_BET * kC + lane] = bs;
+            sm.gate[GATE_NBET * kC + lane] = -bs;
+            sm.gate[GATE_ONE * kC + lane] = 1.f;
             sm.gate[GATE_KDEC * kC + lane] = expf(G_last - Gc);
         }
         __builtin_amdgcn_wave_barrier();   // the table is written before any lane reads it
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int t = wv + NW * j;
-            if (t >= 10) continue;
+        // Branch-free per tile (the N or P choice is a select), so that the unrolled
+        // tiles form one block the compiler can overlap.
+        auto tile = [&](int j) __attribute__((always_inline)) {
+            const int u = wv + NW * j;
+            if (NW * TPW > 20 && j == TPW - 1 && u >= 20) return;
+            const bool isp = u >= 10;                         // uniform
+            const int t = isp ? u - 10 : u;
             const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-            const f32x4 kk = row_tile<DK>(sm.k + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
+            const f32x4 x = row_tile<DK>((isp ? sm.q : sm.k) + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
+            float* dst = isp ? sm.p : sm.a;
+            const float* fac = sm.gate + (isp ? GATE_ONE : GATE_NBET) * kC;   // 1 or -beta
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                sm.a[r * SM::ALD + s] = s < r ? -(sm.gate[GATE_BET * kC + r] * kk[i] *
-                                                  expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]))
-                                              : 0.f;
+                const float d = expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]);
+                // zero outside the triangle by a bit mask (a select there becomes a branch
+                // around the exponential)
+                const unsigned keep = s < r + (int)isp ? ~0u : 0u;
+                dst[r * SM::ALD + s] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, fac[r] * x[i] * d) & keep);
             }
+        };
+        if constexpr (TPW <= 5) {
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) tile(j);
+        } else {                              // two waves: ten tiles each, not unrolled
+#pragma unroll 1
+            for (int j = 0; j < TPW; ++j) tile(j);
         }
-        dev::lds_barrier();   // N is complete
+        dev::lds_barrier();   // N and P are complete
 
         // ---- phase 2: the first wave inverts the diagonal blocks, T_bb = (I + A_bb)^-1 in
         //      place of N_bb, by forward substitution (lane 16 b + j owns column j of
-        //      block b), and forms one P tile; the other waves form the other P tiles
-        //      (P = Q K^T o D, lower tiles); then every wave forms Z = K S and
-        //      R = beta (V - gamma Z) for its strip
+        //      block b); every wave forms Z = K S and R = beta (V - gamma Z) for its
+        //      strip
         if (wv == 0) {
             const int b = g4, j = li;
             const float* Nb = sm.a + (16 * b) * SM::ALD + 16 * b;
@@ -331,18 +336,6 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
             float* Tb = sm.a + (16 * b) * SM::ALD + 16 * b;
 #pragma unroll
             for (int r = 0; r < 16; ++r) Tb[r * SM::ALD + j] = t[r];
-        }
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-            const int t = p_tile<NW>(wv, j);
-            if (t >= 10) continue;
-            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
-            const f32x4 aq = row_tile<DK>(sm.q + (16 * mt + li) * SM::QLD, sm.k + (16 * nt + li) * SM::QLD, g4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                sm.p[r * SM::PLD + s] = s <= r ? aq[i] * expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]) : 0.f;
-            }
         }
         // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
 #pragma unroll
@@ -366,7 +359,7 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
                 for (int i = 0; i < 4; ++i) Racc[mt][nt][i] = bet[i] * fmaf(-gam[i], Zacc[mt][i], Racc[mt][nt][i]);
             }
         }
-        dev::lds_barrier();   // the T_bb and P are complete
+        dev::lds_barrier();   // the T_bb are complete
 
         // ---- phase 3: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
         //      right-looking: once U_i exists it enters every later X_k.  X_i's

@@ -384,7 +384,9 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
                         Racc[k][nt] = mma(sm.a[(16 * k + li) * SM::ALD + 16 * i + 4 * g4 + kk], Uacc[i][nt][kk], Racc[k][nt]);
         }
 
-        // ---- O = gamma o (Q S) + P U, one 16-column tile at a time
+        // ---- O = gamma o (Q S) + P U, one 16-column tile at a time; the chunk's output
+        //      rows as a raw buffer, whose range check drops the stores of rows past L
+        const rsrc_t ro = rows_rsrc(og + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 4);
         const float* gam = sm.gate + GATE_GAM * kC;
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g4 + i;
-                    if (r < L) og[((size_t)(tok + r) * a.H_v + h) * DV + col0 + 16 * nt + li] = a.scale * Oacc[mt][i];
+                    const uint32_t off = (uint32_t)((16 * mt + 4 * g4 + i) * a.H_v * DV + 16 * nt + li) * 4u;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, a.scale * Oacc[mt][i]), ro, (int)off, 0, 0);
                 }
         }
 

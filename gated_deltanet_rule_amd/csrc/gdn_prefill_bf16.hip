@@ -189,6 +189,7 @@ __device__ __forceinline__ f16x4 ld4_tr(const _Float16* p) {
 // (16 cycles per wave and kilobyte against 4 to 8, in a probe that reads the Q/K row
 // fragments below).  A volatile read is never paired.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile u32x2 lds_vu32x2;
 __device__ __forceinline__ f16x4 ld4h_single(const _Float16* p) {
     const u32x2 w = *(lds_vu32x2*)(p);
@@ -665,7 +666,9 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
 
         // ---- phase 3: U_i = T_ii (R_i - sum_{j<i} A_ij U_j); O row block i as soon as
         //      U_0..U_i exist; then the state update
-        __bf16* obase = og + ((size_t)tok * a.H_v + h) * DV + col0;   // uniform
+        // the chunk's output rows of this strip as a raw buffer: its range check drops
+        // the stores of rows past L
+        const rsrc_t ro = rows_rsrc(og + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 2);
         const int bo = li * SM::BLD + 4 * g4;   // the lane's offset in a 16x16 block
         f16x4 Uh[4][NTL], Ul[4][NTL];             // U blocks as fp16 hi + lo pairs; hi alone in
                                               // the output product
@@ -732,20 +735,20 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
             // the nt = 1 columns 12 + 4 g4 .. 12 + 4 g4 + 7: one 16-byte store per lane.
             // A 16-column strip stores its four columns per lane as they are.
             if constexpr (NTL == 1) {
-                const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][0], bf16x4));
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_convertvector(Oacc[i][0], bf16x4));
                 const int r = 16 * i + li;
                 const uint32_t off = (uint32_t)(r * a.H_v * DV + 4 * g4) * 2u;
-                if (r < L) *reinterpret_cast<uint2*>(reinterpret_cast<char*>(obase) + off) = x;
+                __builtin_amdgcn_raw_buffer_store_b64(x, ro, (int)off, 0, 0);
             } else {
                 const uint2 x = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][0], bf16x4));
                 const uint2 y = __builtin_bit_cast(uint2, __builtin_convertvector(Oacc[i][1], bf16x4));
                 const auto s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
                 const auto s1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
-                const uint4 w = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
                 const int r = 16 * i + li;
                 const int col = (g4 & 1) ? 12 + 4 * g4 : 4 * g4;
                 const uint32_t off = (uint32_t)(r * a.H_v * DV + col) * 2u;
-                if (r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(obase) + off) = w;
+                __builtin_amdgcn_raw_buffer_store_b128(w, ro, (int)off, 0, 0);
             }
         }
 

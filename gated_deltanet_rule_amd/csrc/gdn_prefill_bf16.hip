@@ -257,11 +257,14 @@ constexpr int waves_per_simd() {
 
 // SW is the width of a wave's strip of value columns: 32, or 16 for calls whose
 // workgroups each get a compute unit of their own (twice the waves per head, half the
-// work per wave along the chain of chunks).
-template <int DK, int DV, int HG, int KB, int SW>
-__global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>())) void chunk_kernel(PrefillArgs a) {
+// work per wave along the chain of chunks).  CS splits a head's d_v columns over that
+// many workgroups (2 for calls with at most half as many chains as compute units):
+// each repeats the head's shared tiles and solves its own strips, one wave per SIMD.
+template <int DK, int DV, int HG, int KB, int SW, int CS>
+__global__ __launch_bounds__(HG * DV / (SW * CS) * 64, (waves_per_simd<DV, HG, KB, SW>())) void chunk_kernel(PrefillArgs a) {
     using SM = Smem<DK, DV, HG, KB>;
-    constexpr int NWH = DV / SW;             // waves per value head
+    static_assert(CS == 1 || HG == 1, "column splits are for one head per workgroup");
+    constexpr int NWH = DV / (SW * CS);      // waves per value head
     constexpr int NTL = SW / 16;             // 16-column tiles per strip
     constexpr int NW = HG * NWH;             // waves
     constexpr int NT = NW * 64;              // threads
@@ -286,6 +289,8 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
     // one sequence then share one L2, which holds the g and beta lines they all read.
     unsigned wg = blockIdx.x;
     if ((gridDim.x & 7u) == 0) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
+    const int csel = (int)(wg % CS);         // this workgroup's share of the columns
+    wg /= CS;
     const int seq = (int)wg / (a.H_k * GG);
     const int rem = (int)wg - seq * (a.H_k * GG);
     const int kh = rem / GG;
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
     int lane = tid & 63;
     const int hh = wv / NWH;                 // this wave's head within the group
     const int h = h0 + hh;
-    const int col0 = SW * (wv - hh * NWH);
+    const int col0 = SW * (wv - hh * NWH) + (DV / CS) * csel;
     // The "first" wave of each head (the one that scans the gates and inverts the
     // diagonal blocks) is wave hh of the head, so that the heads' first waves sit on
     // different SIMDs (waves go to SIMDs by index modulo 4).
@@ -852,21 +857,21 @@ __global__ __launch_bounds__(HG * DV / SW * 64, (waves_per_simd<DV, HG, KB, SW>(
     }
 }
 
-template <int DK, int DV, int HG, int SW>
+template <int DK, int DV, int HG, int SW, int CS>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const int G = a.H_v / a.H_k;
-    const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG);
+    const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_k * (unsigned)(G / HG) * CS;
     constexpr int KB = HG == 1 ? 1 : 2;
-    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG, KB, SW>), dim3(blocks), dim3(HG * DV / SW * 64), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<DK, DV, HG, KB, SW, CS>), dim3(blocks), dim3(HG * DV / (SW * CS) * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int HG, int SW>
+template <int HG, int SW, int CS>
 hipError_t launch_dims(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, HG, SW>(a, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, HG, SW>(a, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, HG, SW>(a, stream);
-    return launch_typed<64, 64, HG, SW>(a, stream);
+    if (a.d_k == 128 && a.d_v == 128) return launch_typed<128, 128, HG, SW, CS>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_typed<128, 64, HG, SW, CS>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_typed<64, 128, HG, SW, CS>(a, stream);
+    return launch_typed<64, 64, HG, SW, CS>(a, stream);
 }
 
 }  // namespace
@@ -892,15 +897,20 @@ int device_cus() {
 // workgroup runs that chain with four waves on the compute unit instead of eight.
 // When even the (sequence, value head) chains do not outnumber the compute units,
 // each workgroup has a compute unit to itself and its head gets eight waves of
-// 16-column strips, which halves each wave's share of the chain's products.  All
+// 16-column strips, which halves each wave's share of the chain's products; with at
+// most half as many chains as compute units (and d_v = 128), a head's columns go to
+// two workgroups of four such waves, one per SIMD (the shared tiles are formed in
+// both).  All
 // shapes run the same arithmetic per element, so a sequence's results are bitwise
 // the same whichever shape its call takes.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int G = a.H_v / a.H_k;
     const int64_t units = (int64_t)a.num_seqs * a.H_v;   // (sequence, value head) chains
-    if (G % 2 == 0 && units / 2 >= device_cus()) return launch_dims<2, 32>(a, stream);
-    if (units <= device_cus()) return launch_dims<1, 16>(a, stream);
-    return launch_dims<1, 32>(a, stream);
+    if (G % 2 == 0 && units / 2 >= device_cus()) return launch_dims<2, 32, 1>(a, stream);
+    if (a.d_v == 128 && 2 * units <= device_cus())        // four strips per workgroup
+        return a.d_k == 128 ? launch_typed<128, 128, 1, 16, 2>(a, stream) : launch_typed<64, 128, 1, 16, 2>(a, stream);
+    if (units <= device_cus()) return launch_dims<1, 16, 1>(a, stream);
+    return launch_dims<1, 32, 1>(a, stream);
 }
 
 }  // namespace gdn

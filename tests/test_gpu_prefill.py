@@ -157,11 +157,13 @@ def test_prefill_launch_shapes_are_bitwise_equal(dtype, dk, dv):
     """With two value heads per key head the bf16 kernel gives each workgroup both
     heads when the call has enough (sequence, key head) pairs to fill the compute
     units, one head with 32-column strips when its (sequence, value head) chains
-    outnumber the compute units, and one head with 16-column strips otherwise.  The
-    same sequences alone (16-column strips), in a middling batch (32-column strips, one
-    head) and inside a batch that fills the GPU (two heads per workgroup) give bitwise
-    equal outputs, final states and exports.  The fp32 kernel has one head per
-    workgroup and the two strip widths, chosen the same way."""
+    outnumber the compute units, one head with 16-column strips when they do not, and
+    (d_v 128) half a head's strips when the chains are at most half the compute units.
+    The same sequences alone (half heads at d_v 128, else 16-column strips), in a batch
+    of as many chains as compute units (16-column strips), in a middling batch
+    (32-column strips, one head) and inside a batch that fills the GPU (two heads per
+    workgroup) give bitwise equal outputs, final states and exports.  The fp32 kernel
+    has one head per workgroup and the two strip widths, chosen the same way."""
     H_k, H_v = 16, 32
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = -(-cus // H_k)                               # sequences for a full launch of head pairs
@@ -190,24 +192,27 @@ def test_prefill_launch_shapes_are_bitwise_equal(dtype, dk, dv):
         assert torch.equal(dsolo["pool"][2 * n + 3], dbase["pool"][int(base.final_slot[i])]), i
         n_i = offs[i + 1] - offs[i]
         assert torch.equal(exp_solo[:n_i], exp_all[offs[i]:offs[i + 1]]), i
-    # the first m sequences: more chains than compute units, fewer head pairs
-    m = cus // H_v + 1
+    # the first m sequences: as many chains as compute units (16-column strips), then
+    # more chains than compute units and fewer head pairs (32-column strips)
+    m16, m = cus // H_v, cus // H_v + 1
+    assert cus < 2 * m16 * H_v <= 2 * cus
     assert m * H_v > cus and m * H_k < cus and m < n
-    mid = W.make_workload("shape2", seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths[:m],
-                          num_slots=2 * n + 4, export_grid=64)
-    b = int(cu[m])
-    for name in ("q", "k", "v", "g", "beta"):
-        setattr(mid, name, getattr(base, name)[:b].copy())
-    mid.pool = base.pool
-    mid.init_slot = base.init_slot[:m].copy()
-    mid.final_slot = base.final_slot[:m].copy()
-    dmid = to_device(mid)
-    exp_mid, _ = run_prefill(mid, dmid)
-    torch.cuda.synchronize()
-    assert torch.equal(dmid["o"], dbase["o"][:b])
-    fin = torch.as_tensor(mid.final_slot, device=dmid["pool"].device).long()
-    assert torch.equal(dmid["pool"][fin], dbase["pool"][fin])
-    assert torch.equal(exp_mid[:offs[m]], exp_all[:offs[m]])
+    for tag, mm in (("shape16", m16), ("shape2", m)):
+        mid = W.make_workload(tag, seed=33, H_k=H_k, H_v=H_v, d_k=dk, d_v=dv, dtype=dtype, lengths=lengths[:mm],
+                              num_slots=2 * n + 4, export_grid=64)
+        b = int(cu[mm])
+        for name in ("q", "k", "v", "g", "beta"):
+            setattr(mid, name, getattr(base, name)[:b].copy())
+        mid.pool = base.pool
+        mid.init_slot = base.init_slot[:mm].copy()
+        mid.final_slot = base.final_slot[:mm].copy()
+        dmid = to_device(mid)
+        exp_mid, _ = run_prefill(mid, dmid)
+        torch.cuda.synchronize()
+        assert torch.equal(dmid["o"], dbase["o"][:b]), tag
+        fin = torch.as_tensor(mid.final_slot, device=dmid["pool"].device).long()
+        assert torch.equal(dmid["pool"][fin], dbase["pool"][fin]), tag
+        assert torch.equal(exp_mid[:offs[mm]], exp_all[:offs[mm]]), tag
     # and the full batch against the oracle
     check_prefill(base, prefill_reference(base), dbase["o"], dbase["pool"], exp_all)
 

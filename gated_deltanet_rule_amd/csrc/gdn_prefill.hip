@@ -131,10 +131,14 @@ struct ScanSmem {
 // SW is the width of a wave's strip of value columns: 32, or 16 for calls whose
 // workgroups each get a compute unit of their own (twice the waves, half the products
 // per wave along the chain of chunks).
-template <int DK, int DV, int SW>
-__global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
+// NX helper waves (0 or 4) join a workgroup of four strips: they share the tiles and
+// invert the diagonal blocks, and sit out the strips' work.
+template <int DK, int DV, int SW, int NX>
+__global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a) {
     using SM = ScanSmem<DK, DV>;
-    constexpr int NW = DV / SW;              // waves (one strip each)
+    constexpr int NWS = DV / SW;             // strip waves (one strip each)
+    constexpr int NW = NWS + NX;             // waves
+    constexpr int SUBW = NX > 0 ? NWS : 0;   // the wave that inverts the diagonal blocks
     constexpr int NTL = SW / 16;             // 16-column tiles per strip
     constexpr int NT = NW * 64;              // threads
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
@@ -158,13 +162,14 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
     int lane = tid & 63;
-    const int col0 = SW * wv;
+    const bool strip = wv < NWS;             // uniform
+    const int col0 = SW * wv;                // (strip waves)
 
     const size_t SE = (size_t)DK * DV;
     // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
     f32x4 Sacc[MT_S][NTL];
     const int isl = a.init_slot ? a.init_slot[seq] : -1;
-    if (isl >= 0 && isl < a.num_slots) {
+    if (strip && isl >= 0 && isl < a.num_slots) {
         const int li = lane & 15, g4 = lane >> 4;
         const float* src = a.pool + ((size_t)isl * a.H_v + h) * SE;
 #pragma unroll
@@ -265,13 +270,15 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         //      as N = -A at once, zeros on and above the diagonal; nothing reads the
         //      upper tiles) and then the ten of P = Q K^T o D, round robin
         f32x4 Racc[4][NTL];          // V, then R = beta (V - gamma Z), then X_i of the solve
+        if (strip) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+                for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Racc[mt][nt][i] = sm.v[(16 * mt + 4 * g4 + i) * SM::VLD + col0 + 16 * nt + li];
+                    for (int i = 0; i < 4; ++i)
+                        Racc[mt][nt][i] = sm.v[(16 * mt + 4 * g4 + i) * SM::VLD + col0 + 16 * nt + li];
+        }
         {
             const float gs = sm.graw[lane];
             const float bs = sm.braw[lane];
@@ -315,11 +322,11 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
         }
         dev::lds_barrier();   // N and P are complete
 
-        // ---- phase 2: the first wave inverts the diagonal blocks, T_bb = (I + A_bb)^-1 in
-        //      place of N_bb, by forward substitution (lane 16 b + j owns column j of
-        //      block b); every wave forms Z = K S and R = beta (V - gamma Z) for its
-        //      strip
-        if (wv == 0) {
+        // ---- phase 2: one wave (the first helper, else the first) inverts the diagonal
+        //      blocks, T_bb = (I + A_bb)^-1 in place of N_bb, by forward substitution
+        //      (lane 16 b + j owns column j of block b); every strip wave forms Z = K S
+        //      and R = beta (V - gamma Z) for its strip
+        if (wv == SUBW) {
             const int b = g4, j = li;
             const float* Nb = sm.a + (16 * b) * SM::ALD + 16 * b;
             // each row starts from column j of I: rows above j then sum products with
@@ -337,147 +344,151 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) Tb[r * SM::ALD + j] = t[r];
         }
-        // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
+        if (strip) {
+            // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-            __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
-            f32x4 Zacc[4];
+            for (int nt = 0; nt < NTL; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
+                f32x4 Zacc[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) Zacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < 4; ++mt) Zacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KS_DK; ++kk) {
-                const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    Zacc[mt] = mma(sm.k[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Zacc[mt]);
-            }
+                    for (int mt = 0; mt < 4; ++mt)
+                        Zacc[mt] = mma(sm.k[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Zacc[mt]);
+                }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 gam = *reinterpret_cast<const f32x4*>(sm.gate + GATE_GAM * kC + 16 * mt + 4 * g4);
-                const f32x4 bet = *reinterpret_cast<const f32x4*>(sm.gate + GATE_BET * kC + 16 * mt + 4 * g4);
+                for (int mt = 0; mt < 4; ++mt) {
+                    const f32x4 gam = *reinterpret_cast<const f32x4*>(sm.gate + GATE_GAM * kC + 16 * mt + 4 * g4);
+                    const f32x4 bet = *reinterpret_cast<const f32x4*>(sm.gate + GATE_BET * kC + 16 * mt + 4 * g4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Racc[mt][nt][i] = bet[i] * fmaf(-gam[i], Zacc[mt][i], Racc[mt][nt][i]);
+                    for (int i = 0; i < 4; ++i) Racc[mt][nt][i] = bet[i] * fmaf(-gam[i], Zacc[mt][i], Racc[mt][nt][i]);
+                }
             }
         }
         dev::lds_barrier();   // the T_bb are complete
 
-        // ---- phase 3: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
-        //      right-looking: once U_i exists it enters every later X_k.  X_i's
-        //      accumulator feeds the products as their B operand (from-C order).
-        f32x4 Uacc[4][NTL];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    u = mma(sm.a[(16 * i + li) * SM::ALD + 16 * i + 4 * g4 + kk], Racc[i][nt][kk], u);
-                Uacc[i][nt] = u;
-            }
-#pragma unroll
-            for (int k = i + 1; k < 4; ++k)
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        Racc[k][nt] = mma(sm.a[(16 * k + li) * SM::ALD + 16 * i + 4 * g4 + kk], Uacc[i][nt][kk], Racc[k][nt]);
-        }
-
-        // ---- O = gamma o (Q S) + P U, one 16-column tile at a time; the chunk's output
-        //      rows as a raw buffer, whose range check drops the stores of rows past L
-        const rsrc_t ro = rows_rsrc(og + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 4);
-        const float* gam = sm.gate + GATE_GAM * kC;
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 Oacc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS_DK; ++kk) {
-                const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    Oacc[mt] = mma(sm.q[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Oacc[mt]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gam[16 * mt + 4 * g4 + i];
-#pragma unroll
-            for (int kk = 0; kk < KS_C; ++kk) {
-                const float ub = acc_fromc(&Uacc[0][nt], kk, NTL);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    if (16 * (kk >> 2) > 16 * mt + 15) continue;  // P is lower triangular
-                    Oacc[mt] = mma(sm.p[(16 * mt + li) * SM::PLD + k_fromc(kk, g4)], ub, Oacc[mt]);
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t off = (uint32_t)((16 * mt + 4 * g4 + i) * a.H_v * DV + 16 * nt + li) * 4u;
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, a.scale * Oacc[mt][i]), ro, (int)off, 0, 0);
-                }
-        }
-
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- S = gamma_last S + K^T (diag(e^(G_last - G)) U)
-        const float gl_last = gam[kC - 1];
-        const float* kdec = sm.gate + GATE_KDEC * kC;
-#pragma unroll
-        for (int mt = 0; mt < MT_S; ++mt)
+        if (strip) {
+            // ---- phase 3: the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
+            //      right-looking: once U_i exists it enters every later X_k.  X_i's
+            //      accumulator feeds the products as their B operand (from-C order).
+            f32x4 Uacc[4][NTL];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt][i] *= gl_last;
+                for (int nt = 0; nt < NTL; ++nt) {
+                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        u = mma(sm.a[(16 * i + li) * SM::ALD + 16 * i + 4 * g4 + kk], Racc[i][nt][kk], u);
+                    Uacc[i][nt] = u;
+                }
+#pragma unroll
+                for (int k = i + 1; k < 4; ++k)
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            Racc[k][nt] = mma(sm.a[(16 * k + li) * SM::ALD + 16 * i + 4 * g4 + kk], Uacc[i][nt][kk], Racc[k][nt]);
             }
-#pragma unroll
-        for (int kk = 0; kk < KS_C; ++kk) {
-            const float d = kdec[k_fromc(kk, g4)];
-            float ub[NTL];
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) ub[nt] = acc_fromc(&Uacc[0][nt], kk, NTL) * d;
-#pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-                const float ka = sm.k[k_fromc(kk, g4) * SM::QLD + 16 * mt + li];
-#pragma unroll
-                for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = mma(ka, ub[nt], Sacc[mt][nt]);
-            }
-        }
 
-        // ---- export on the grid
-        if (a.export_grid > 0) {
-            const int64_t p_end = pos0 + e0;
-            if (p_end % a.export_grid == 0) {
-                const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
-                const int64_t idx = (int64_t)a.export_offsets[seq] + m;
-                float* dst = nullptr;
-                if (idx >= 0 && idx < a.export_capacity) {
-                    if (!a.export_slots) {
-                        dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
-                    } else {                    // straight into a cache slot
-                        const int sl = a.export_slots[idx];
-                        if (sl >= 0 && sl < a.num_slots) dst = a.pool + ((size_t)sl * a.H_v + h) * SE;
+            // ---- O = gamma o (Q S) + P U, one 16-column tile at a time; the chunk's output
+            //      rows as a raw buffer, whose range check drops the stores of rows past L
+            const rsrc_t ro = rows_rsrc(og + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 4);
+            const float* gam = sm.gate + GATE_GAM * kC;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 Oacc[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        Oacc[mt] = mma(sm.q[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Oacc[mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gam[16 * mt + 4 * g4 + i];
+#pragma unroll
+                for (int kk = 0; kk < KS_C; ++kk) {
+                    const float ub = acc_fromc(&Uacc[0][nt], kk, NTL);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        if (16 * (kk >> 2) > 16 * mt + 15) continue;  // P is lower triangular
+                        Oacc[mt] = mma(sm.p[(16 * mt + li) * SM::PLD + k_fromc(kk, g4)], ub, Oacc[mt]);
                     }
                 }
-                if (dst) {
 #pragma unroll
-                    for (int mt = 0; mt < MT_S; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                        for (int nt = 0; nt < NTL; ++nt)
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t off = (uint32_t)((16 * mt + 4 * g4 + i) * a.H_v * DV + 16 * nt + li) * 4u;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, a.scale * Oacc[mt][i]), ro, (int)off, 0, 0);
+                    }
+            }
+
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- S = gamma_last S + K^T (diag(e^(G_last - G)) U)
+            const float gl_last = gam[kC - 1];
+            const float* kdec = sm.gate + GATE_KDEC * kC;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
+            for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt][i] *= gl_last;
+                }
+#pragma unroll
+            for (int kk = 0; kk < KS_C; ++kk) {
+                const float d = kdec[k_fromc(kk, g4)];
+                float ub[NTL];
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) ub[nt] = acc_fromc(&Uacc[0][nt], kk, NTL) * d;
+#pragma unroll
+                for (int mt = 0; mt < MT_S; ++mt) {
+                    const float ka = sm.k[k_fromc(kk, g4) * SM::QLD + 16 * mt + li];
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = mma(ka, ub[nt], Sacc[mt][nt]);
+                }
+            }
+
+            // ---- export on the grid
+            if (a.export_grid > 0) {
+                const int64_t p_end = pos0 + e0;
+                if (p_end % a.export_grid == 0) {
+                    const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
+                    const int64_t idx = (int64_t)a.export_offsets[seq] + m;
+                    float* dst = nullptr;
+                    if (idx >= 0 && idx < a.export_capacity) {
+                        if (!a.export_slots) {
+                            dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                        } else {                    // straight into a cache slot
+                            const int sl = a.export_slots[idx];
+                            if (sl >= 0 && sl < a.num_slots) dst = a.pool + ((size_t)sl * a.H_v + h) * SE;
+                        }
+                    }
+                    if (dst) {
+#pragma unroll
+                        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+                            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
+                    }
                 }
             }
         }
     }
 
     const int fsl = a.final_slot ? a.final_slot[seq] : -1;
-    if (fsl >= 0 && fsl < a.num_slots) {
+    if (strip && fsl >= 0 && fsl < a.num_slots) {
         const int li = lane & 15, g4 = lane >> 4;
         float* dst = a.pool + ((size_t)fsl * a.H_v + h) * SE;
 #pragma unroll
@@ -493,7 +504,10 @@ __global__ __launch_bounds__(DV / SW * 64) void scan_kernel(PrefillArgs a) {
 template <int DK, int DV, int SW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_v;
-    hipLaunchKernelGGL((scan_kernel<DK, DV, SW>), dim3(blocks), dim3(DV / SW * 64), 0, stream, a);
+    // four helper waves beside four 16-column strips (d_v 64): a compute unit of its
+    // own then runs two waves per SIMD
+    constexpr int NX = SW == 16 && DV == 64 ? 4 : 0;
+    hipLaunchKernelGGL((scan_kernel<DK, DV, SW, NX>), dim3(blocks), dim3((DV / SW + NX) * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -138,7 +138,7 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
     using SM = ScanSmem<DK, DV>;
     constexpr int NWS = DV / SW;             // strip waves (one strip each)
     constexpr int NW = NWS + NX;             // waves
-    constexpr int SUBW = NX > 0 ? NWS : 0;   // the wave that inverts the diagonal blocks
+    constexpr int SUBW = 0;                  // the wave that inverts the diagonal blocks
     constexpr int NTL = SW / 16;             // 16-column tiles per strip
     constexpr int NT = NW * 64;              // threads
     constexpr int MT_S = DK / 16;            // 16-row tiles of the state
@@ -162,8 +162,11 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
     int lane = tid & 63;
-    const bool strip = wv < NWS;             // uniform
-    const int col0 = SW * wv;                // (strip waves)
+    // Helpers are the first waves: waves wv and wv + 4 share a SIMD, and the older wave
+    // wins the issue arbitration, so the helper's substitution runs ahead of its SIMD
+    // partner's Z products.
+    const bool strip = NX == 0 || wv >= NX;  // uniform
+    const int col0 = SW * (wv - NX);         // (strip waves)
 
     const size_t SE = (size_t)DK * DV;
     // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
@@ -322,7 +325,7 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
         }
         dev::lds_barrier();   // N and P are complete
 
-        // ---- phase 2: one wave (the first helper, else the first) inverts the diagonal
+        // ---- phase 2: the first wave (a helper, if any) inverts the diagonal
         //      blocks, T_bb = (I + A_bb)^-1 in place of N_bb, by forward substitution
         //      (lane 16 b + j owns column j of block b); every strip wave forms Z = K S
         //      and R = beta (V - gamma Z) for its strip

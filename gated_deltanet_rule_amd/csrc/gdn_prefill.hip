@@ -71,6 +71,21 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ int k_fromc(int ks, int g) { return 16 * (ks >> 2) + 4 * g + (ks & 3); }
+// e^x as 2^(x log2 e): log2 e split into an fp32 part and the remainder (Cody and
+// Waite's argument splitting), so that t + tl carries x log2 e to about 2^-48 of it;
+// the hardware base-2 exponential of t, and 2^tl ~ 1 + tl ln 2 for the tiny tl.  About
+// 1-2 ulp; results below fp32's normal range lose precision (the decays there are
+// negligible against the unit-sized terms they sit beside).
+__device__ __forceinline__ float exp_fast(float x) {
+    constexpr float kL2eHi = 1.44269502162933349609375f;
+    constexpr float kL2eLo = 1.925963033500011079e-08f;
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float t = x * kL2eHi;
+    const float tl = fmaf(x, kL2eHi, -t) + x * kL2eLo;
+    const float p = __builtin_amdgcn_exp2f(t);
+    return fmaf(p * tl, kLn2, p);
+}
+
 // element k of a C-layout tile set (tiles[t * stride] holds rows 16 t ..), from-C order
 __device__ __forceinline__ float acc_fromc(const f32x4* tiles, int ks, int stride) {
     return tiles[(ks >> 2) * stride][ks & 3];
@@ -288,11 +303,11 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
             const float Gc = dev::wave_inclusive_sum(gs);
             const float G_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gc), kC - 1));
             sm.gate[GATE_G * kC + lane] = Gc;
-            sm.gate[GATE_GAM * kC + lane] = expf(Gc);
+            sm.gate[GATE_GAM * kC + lane] = exp_fast(Gc);
             sm.gate[GATE_BET * kC + lane] = bs;
             sm.gate[GATE_NBET * kC + lane] = -bs;
             sm.gate[GATE_ONE * kC + lane] = 1.f;
-            sm.gate[GATE_KDEC * kC + lane] = expf(G_last - Gc);
+            sm.gate[GATE_KDEC * kC + lane] = exp_fast(G_last - Gc);
         }
         __builtin_amdgcn_wave_barrier();   // the table is written before any lane reads it
         // Branch-free per tile (the N or P choice is a select), so that the unrolled
@@ -309,7 +324,7 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
-                const float d = expf(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]);
+                const float d = exp_fast(sm.gate[GATE_G * kC + r] - sm.gate[GATE_G * kC + s]);
                 // zero outside the triangle by a bit mask (a select there becomes a branch
                 // around the exponential)
                 const unsigned keep = s < r + (int)isp ? ~0u : 0u;

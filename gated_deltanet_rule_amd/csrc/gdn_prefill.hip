@@ -519,12 +519,404 @@ __global__ __launch_bounds__((DV / SW + NX) * 64) void scan_kernel(PrefillArgs a
     }
 }
 
+// d_k = d_v = 64 in 16-column strips: the four strip waves (4-7) and four helper waves
+// (0-3) work a chunk apart.  While the strips run chunk c's solve, output and state
+// update, the helpers stage chunk c + 1 and form its tiles and diagonal inverses
+// (helper b block b's diagonal K K^T tile and its inverse, so the helpers need no sync
+// among themselves, then four of the sixteen other tiles).  Q, K, N, P and the gate
+// table are double-buffered by chunk parity; the strips read V straight from HBM.
+// Every wave runs the same two barriers per chunk, in straight-line code.  The
+// arithmetic per element is the scan kernel's.
+template <int DK, int DV>
+struct PipeSmem {
+    static constexpr int QLD = DK + 4;        // Q and K rows
+    static constexpr int ALD = kC + 4;        // N / T rows
+    static constexpr int PLD = ALD;           // P rows
+    float q[2][kC * QLD];
+    float k[2][kC * QLD];
+    float a[2][kC * ALD];
+    float p[2][kC * PLD];
+    float gate[2][kGates * kC];
+};
+
+__device__ __forceinline__ float ld4_rows(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+__global__ __launch_bounds__(512) void scan_kernel_pipe(PrefillArgs a) {
+    constexpr int DK = 64, DV = 64, SW = 16, NX = 4;
+    using SM = PipeSmem<DK, DV>;
+    constexpr int NTL = 1;                   // 16-column tiles per strip
+    constexpr int MT_S = DK / 16;            // 16-row tiles of the state
+    constexpr int KS_DK = DK / 4;            // k steps over d_k
+    constexpr int KS_C = kC / 4;             // k steps over the chunk
+    constexpr int VPR = DK / 4;              // 16-byte vectors per Q/K row
+    constexpr int NTH = NX * 64;             // helper threads
+    constexpr int NPF = 2 * kC * VPR / NTH;  // prefetched Q/K vectors per helper thread
+    static_assert(NPF * NTH == 2 * kC * VPR && (kC * VPR) % NTH == 0, "Q/K prefetch must divide evenly");
+    __shared__ __attribute__((aligned(16))) SM sm;
+
+    const int G = a.H_v / a.H_k;
+    const int seq = blockIdx.x / a.H_v;
+    const int h = blockIdx.x - seq * a.H_v;
+    const int kh = h / G;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+    int lane = tid & 63;
+    const bool strip = wv >= NX;             // uniform
+    const int col0 = SW * (wv - NX);         // (strip waves)
+
+    const size_t SE = (size_t)DK * DV;
+    // state strip in accumulator layout: Sacc[mt][nt] holds S[16mt + 4g + i][col0 + 16nt + li]
+    f32x4 Sacc[MT_S][NTL];
+    const int isl = a.init_slot ? a.init_slot[seq] : -1;
+    if (strip && isl >= 0 && isl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
+        const float* src = a.pool + ((size_t)isl * a.H_v + h) * SE;
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sacc[mt][0][i] = src[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + li];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt) Sacc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int lo, len;
+    dev::seq_range(a.cu_seqlens, seq, a.total_tokens, lo, len);
+    const int64_t pos0 = a.start_pos ? a.start_pos[seq] : 0;
+    const int off64 = (int)(pos0 & (kC - 1));
+    const int nchunks = dev::seq_chunks(len, off64);
+
+    const float* qg = static_cast<const float*>(a.q);
+    const float* kg = static_cast<const float*>(a.k);
+    const float* vg = static_cast<const float*>(a.v);
+    float* og = static_cast<float*>(a.o);
+
+    // helpers: a chunk's Q and K rows (16-byte vectors) and, on the first helper, its g
+    // and beta (lane = token)
+    uint4 pf[NPF];
+    float gpf = 0.f, bpf = 0.f;
+    auto prefetch_h = [&](int c, int t) __attribute__((always_inline)) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const rsrc_t rq = rows_rsrc(qg + (size_t)tok * a.H_k * DK, L * a.H_k * DK * 4);
+        const rsrc_t rk = rows_rsrc(kg + (size_t)tok * a.H_k * DK, L * a.H_k * DK * 4);
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int i = t + NTH * j;
+            const int which = NTH * j / (kC * VPR);      // 0: Q, 1: K (uniform)
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            const uint32_t off = (uint32_t)((r * a.H_k + kh) * DK + vi * 4) * 4u;
+            pf[j] = ld16_rows(which == 0 ? rq : rk, off);
+        }
+        if (t < kC) {
+            const uint32_t off = (uint32_t)(t * a.H_v + h) * 4u;
+            gpf = ld4_rows(rows_rsrc(a.g + (size_t)tok * a.H_v, L * a.H_v * 4), off);
+            bpf = ld4_rows(rows_rsrc(a.beta + (size_t)tok * a.H_v, L * a.H_v * 4), off);
+        }
+    };
+    // helpers: the prefetched chunk into buffer nb; the first helper scans its gates
+    auto stage_h = [&](int nb, int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int i = t + NTH * j;
+            const int which = i / (kC * VPR);
+            const int r = (i / VPR) % kC, vi = i % VPR;
+            *reinterpret_cast<uint4*>((which == 0 ? sm.q[nb] : sm.k[nb]) + r * SM::QLD + vi * 4) = pf[j];
+        }
+        if (wv == 0) {
+            float* gt = sm.gate[nb];
+            const float Gc = dev::wave_inclusive_sum(gpf);
+            const float G_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gc), kC - 1));
+            gt[GATE_G * kC + t] = Gc;
+            gt[GATE_GAM * kC + t] = exp_fast(Gc);
+            gt[GATE_BET * kC + t] = bpf;
+            gt[GATE_NBET * kC + t] = -bpf;
+            gt[GATE_ONE * kC + t] = 1.f;
+            gt[GATE_KDEC * kC + t] = exp_fast(G_last - Gc);
+        }
+    };
+    // strips: a chunk's V strip in accumulator layout, rows past the chunk as zeros
+    float vpf[4 * MT_S];
+    auto prefetch_v = [&](int c, int ln) __attribute__((always_inline)) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const rsrc_t rv = rows_rsrc(vg + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 4);
+        const unsigned li = (unsigned)ln & 15u, g4 = (unsigned)ln >> 4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vpf[4 * mt + i] = ld4_rows(rv, (uint32_t)((16 * mt + 4 * g4 + i) * a.H_v * DV + li) * 4u);
+    };
+    // helpers: chunk n's tiles and diagonal inverses into buffer nb (helper b: block b's
+    // diagonal K K^T tile and its inverse, then four of the sixteen other tiles)
+    auto tiles_h = [&](int nb, int li, int g4) __attribute__((always_inline)) {
+        const float* Q_ = sm.q[nb];
+        const float* K_ = sm.k[nb];
+        const float* GT_ = sm.gate[nb];
+        float* A_ = sm.a[nb];
+        float* P_ = sm.p[nb];
+        auto tile = [&](int u) __attribute__((always_inline)) {
+            const bool isp = u >= 10;                         // uniform
+            const int t = isp ? u - 10 : u;
+            const int mt = (t >= 1) + (t >= 3) + (t >= 6), nt = t - mt * (mt + 1) / 2;
+            const f32x4 x = row_tile<DK>((isp ? Q_ : K_) + (16 * mt + li) * SM::QLD, K_ + (16 * nt + li) * SM::QLD, g4);
+            float* dst = isp ? P_ : A_;
+            const float* fac = GT_ + (isp ? GATE_ONE : GATE_NBET) * kC;   // 1 or -beta
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g4 + i, s = 16 * nt + li;
+                const float d = exp_fast(GT_[GATE_G * kC + r] - GT_[GATE_G * kC + s]);
+                const unsigned keep = s < r + (int)isp ? ~0u : 0u;
+                dst[r * SM::ALD + s] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, fac[r] * x[i] * d) & keep);
+            }
+        };
+        const int b = wv;                    // this helper's diagonal block
+        tile(b * (b + 3) / 2);
+        __builtin_amdgcn_wave_barrier();     // N_bb is written before it is read
+        {   // T_bb = (I + A_bb)^-1 in place of N_bb, lane owning column li (every lane
+            // group the same column: same values to the same addresses)
+            const float* Nb = A_ + (16 * b) * SM::ALD + 16 * b;
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == li ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc = fmaf(Nb[r * SM::ALD + s2], t[s2], acc);
+                t[r] = acc;
+            }
+            __builtin_amdgcn_wave_barrier();
+            float* Tb = A_ + (16 * b) * SM::ALD + 16 * b;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tb[r * SM::ALD + li] = t[r];
+        }
+        // the others: off-diagonal K K^T tiles 1 3 4 6 7 8, then the Q K^T tiles 10..19
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int o = wv + NX * j;
+            tile(o < 6 ? o + 1 + (o >= 1) + (o >= 3) : o + 4);
+        }
+    };
+
+    if (nchunks > 0) {
+        if (!strip) {
+            prefetch_h(0, tid);
+            stage_h(0, tid);
+            if (nchunks > 1) prefetch_h(1, tid);
+        } else {
+            prefetch_v(0, lane);
+        }
+    }
+    if (nchunks > 0) {
+        dev::lds_barrier();                  // chunk 0 staged
+        if (!strip) {
+            const int li = lane & 15, g4 = lane >> 4;
+            tiles_h(0, li, g4);
+        }
+        dev::lds_barrier();                  // chunk 0's tiles and inverses
+    }
+
+    for (int c = 0; c < nchunks; ++c) {
+        int b0, e0;
+        dev::chunk_span(c, off64, len, b0, e0);
+        const int tok = lo + b0, L = e0 - b0;
+        const int cb = c & 1, nb = cb ^ 1;
+        int tid_l = tid;
+        asm volatile("" : "+v"(lane), "+v"(tid_l));
+        const int li = lane & 15, g4 = lane >> 4;
+        const float* Q_ = sm.q[cb];
+        const float* K_ = sm.k[cb];
+        const float* GT_ = sm.gate[cb];
+        const float* A_ = sm.a[cb];
+        const float* P_ = sm.p[cb];
+
+        // ---- first half: the helpers stage chunk c + 1 and fetch chunk c + 2; the strips
+        //      take chunk c's V, fetch chunk c + 1's and form Z = K S and R
+        f32x4 Racc[4][NTL];
+        if (!strip) {
+            if (c + 1 < nchunks) {
+                stage_h(nb, tid_l);
+                if (c + 2 < nchunks) prefetch_h(c + 2, tid_l);
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Racc[mt][0][i] = vpf[4 * mt + i];
+            if (c + 1 < nchunks) prefetch_v(c + 1, lane);
+            // Z = K S and R = beta (V - gamma Z), one 16-column tile at a time
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);   // keep the two tiles' live ranges apart
+                f32x4 Zacc[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) Zacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        Zacc[mt] = mma(K_[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Zacc[mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const f32x4 gam = *reinterpret_cast<const f32x4*>(GT_ + GATE_GAM * kC + 16 * mt + 4 * g4);
+                    const f32x4 bet = *reinterpret_cast<const f32x4*>(GT_ + GATE_BET * kC + 16 * mt + 4 * g4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Racc[mt][nt][i] = bet[i] * fmaf(-gam[i], Zacc[mt][i], Racc[mt][nt][i]);
+                }
+            }
+        }
+        dev::lds_barrier();   // chunk c + 1 staged
+
+        // ---- second half: the helpers form chunk c + 1's tiles and inverses; the strips
+        //      run chunk c's solve, output, state update and export
+        if (!strip) {
+            if (c + 1 < nchunks) tiles_h(nb, li, g4);
+        }
+        if (strip) {
+            // ---- the block solve U_i = T_ii X_i, X_i = R_i + sum_{j<i} N_ij U_j,
+            //      right-looking: once U_i exists it enters every later X_k.  X_i's
+            //      accumulator feeds the products as their B operand (from-C order).
+            f32x4 Uacc[4][NTL];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        u = mma(A_[(16 * i + li) * SM::ALD + 16 * i + 4 * g4 + kk], Racc[i][nt][kk], u);
+                    Uacc[i][nt] = u;
+                }
+#pragma unroll
+                for (int k = i + 1; k < 4; ++k)
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            Racc[k][nt] = mma(A_[(16 * k + li) * SM::ALD + 16 * i + 4 * g4 + kk], Uacc[i][nt][kk], Racc[k][nt]);
+            }
+
+            // ---- O = gamma o (Q S) + P U, one 16-column tile at a time; the chunk's output
+            //      rows as a raw buffer, whose range check drops the stores of rows past L
+            const rsrc_t ro = rows_rsrc(og + ((size_t)tok * a.H_v + h) * DV + col0, L * a.H_v * DV * 4);
+            const float* gam = GT_ + GATE_GAM * kC;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 Oacc[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) Oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS_DK; ++kk) {
+                    const float sb = acc_fromc(&Sacc[0][nt], kk, NTL);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        Oacc[mt] = mma(Q_[(16 * mt + li) * SM::QLD + k_fromc(kk, g4)], sb, Oacc[mt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gam[16 * mt + 4 * g4 + i];
+#pragma unroll
+                for (int kk = 0; kk < KS_C; ++kk) {
+                    const float ub = acc_fromc(&Uacc[0][nt], kk, NTL);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        if (16 * (kk >> 2) > 16 * mt + 15) continue;  // P is lower triangular
+                        Oacc[mt] = mma(P_[(16 * mt + li) * SM::PLD + k_fromc(kk, g4)], ub, Oacc[mt]);
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t off = (uint32_t)((16 * mt + 4 * g4 + i) * a.H_v * DV + 16 * nt + li) * 4u;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, a.scale * Oacc[mt][i]), ro, (int)off, 0, 0);
+                    }
+            }
+
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- S = gamma_last S + K^T (diag(e^(G_last - G)) U)
+            const float gl_last = gam[kC - 1];
+            const float* kdec = GT_ + GATE_KDEC * kC;
+#pragma unroll
+            for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt][i] *= gl_last;
+                }
+#pragma unroll
+            for (int kk = 0; kk < KS_C; ++kk) {
+                const float d = kdec[k_fromc(kk, g4)];
+                float ub[NTL];
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) ub[nt] = acc_fromc(&Uacc[0][nt], kk, NTL) * d;
+#pragma unroll
+                for (int mt = 0; mt < MT_S; ++mt) {
+                    const float ka = K_[k_fromc(kk, g4) * SM::QLD + 16 * mt + li];
+#pragma unroll
+                    for (int nt = 0; nt < NTL; ++nt) Sacc[mt][nt] = mma(ka, ub[nt], Sacc[mt][nt]);
+                }
+            }
+
+            // ---- export on the grid
+            if (a.export_grid > 0) {
+                const int64_t p_end = pos0 + e0;
+                if (p_end % a.export_grid == 0) {
+                    const int64_t m = p_end / a.export_grid - pos0 / a.export_grid - 1;
+                    const int64_t idx = (int64_t)a.export_offsets[seq] + m;
+                    float* dst = nullptr;
+                    if (idx >= 0 && idx < a.export_capacity) {
+                        if (!a.export_slots) {
+                            dst = a.export_states + ((size_t)idx * a.H_v + h) * SE;
+                        } else {                    // straight into a cache slot
+                            const int sl = a.export_slots[idx];
+                            if (sl >= 0 && sl < a.num_slots) dst = a.pool + ((size_t)sl * a.H_v + h) * SE;
+                        }
+                    }
+                    if (dst) {
+#pragma unroll
+                        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+                            for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + 16 * nt + li] = Sacc[mt][nt][i];
+                    }
+                }
+            }
+        }
+        dev::lds_barrier();   // chunk c done; chunk c + 1's tiles complete
+    }
+
+    const int fsl = a.final_slot ? a.final_slot[seq] : -1;
+    if (strip && fsl >= 0 && fsl < a.num_slots) {
+        const int li = lane & 15, g4 = lane >> 4;
+        float* dst = a.pool + ((size_t)fsl * a.H_v + h) * SE;
+#pragma unroll
+        for (int mt = 0; mt < MT_S; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * mt + 4 * g4 + i) * DV + col0 + li] = Sacc[mt][0][i];
+    }
+}
+
 template <int DK, int DV, int SW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const unsigned blocks = (unsigned)a.num_seqs * (unsigned)a.H_v;
     // four helper waves beside four 16-column strips (d_v 64): a compute unit of its
     // own then runs two waves per SIMD
     constexpr int NX = SW == 16 && DV == 64 ? 4 : 0;
+    if constexpr (DK == 64 && DV == 64 && SW == 16) {   // the helpers a chunk ahead
+        hipLaunchKernelGGL(scan_kernel_pipe, dim3(blocks), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((scan_kernel<DK, DV, SW, NX>), dim3(blocks), dim3((DV / SW + NX) * 64), 0, stream, a);
     return hipGetLastError();
 }

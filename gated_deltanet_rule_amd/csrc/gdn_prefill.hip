@@ -20,8 +20,9 @@
 // The solve runs on 16-row blocks: with N = -A and T_ii = (I + A_ii)^-1 (16 x 16),
 //     U_i = T_ii (R_i + sum_{j<i} N_ij U_j).
 //
-// One kernel.  A workgroup owns one sequence and one value head and walks the
-// sequence's chunks in order.  Per value head, d_v is split into 32-column
+// One kernel (for d_k = d_v = 64 in 16-column strips, scan_kernel_pipe below, the same
+// work with the helper waves a chunk ahead).  A workgroup owns one sequence and one
+// value head and walks the sequence's chunks in order.  Per value head, d_v is split into 32-column
 // strips (16-column ones when the call has no more chains than compute units), one
 // wave each; a wave keeps its strip of S (d_k x 32 or d_k x 16, fp32) in MFMA
 // accumulator registers for the whole sequence.  The d_v columns of S, R, U and O are
